@@ -1,0 +1,242 @@
+"""Benchmark: one rank's share of context-parallel ring attention on one MI355X.
+
+A step is one pass of the whole hot path for the rank: zigzag-permute the
+global K and V (all ranks' shares, which the ring visits) and the rank's Q,
+run the rank's ring (N partial-attention launches in ring order, N-1
+online-softmax merges), and scatter O and lse back to global token order.
+Inputs are resident in HBM before timing starts.
+
+Metric: causal-useful attention TFLOP/s = 4 * D * B * H * P / t, where P is the
+number of (query, key) pairs the rank's queries may see (key position <= query
+position), i.e. masked and skipped work is not counted.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (partial
+attention, bf16 MFMA-bound): its useful FLOP per launch over its average launch
+duration, timed with HIP events on the launch stream.  `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same share's query rows.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
+PEAK_HBM_GBS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "partial_attn_128k_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "sequence_attention_cpa_amd", "csrc", "partial_attn.hip")
+
+
+def causal_pairs(q_pos, k_pos):
+    import numpy as np
+    return int(np.searchsorted(np.sort(k_pos), q_pos, side="right").sum())
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic():
+    """HBM bytes per partial launch from committed rocprofv3 counter runs, or
+    None when they were taken on a different version of the kernel."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha") != kernel_sha():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, Q, K, V, pos_rank, seconds):
+    """The oracle, untouched, over a sample of the rank's query rows; rows are
+    independent, so host threads each take whole (head, row-block) tasks."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import cpa_oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    K64 = {bh: K[bh].to(torch.float64).numpy() for bh in heads}
+    V64 = {bh: V[bh].to(torch.float64).numpy() for bh in heads}
+    rng = np.random.default_rng(0)
+    block = 16
+    # sample row blocks from the whole share, timing until the budget is spent
+    tasks = []
+    for _ in range(4096):
+        bh = heads[int(rng.integers(len(heads)))]
+        t0 = int(rng.integers(0, len(pos_rank) - block + 1))
+        tasks.append((bh, pos_rank[t0:t0 + block]))
+
+    def run(task):
+        bh, rows = task
+        q = Q[bh][torch.from_numpy(rows)].to(torch.float64).numpy()
+        cpa_oracle.attention_rows(q, rows, K64[bh], V64[bh], w.causal, block=block)
+        return sum(int(p) + 1 for p in rows) if w.causal else len(rows) * w.L
+
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    pairs = 0
+    done_rows = 0
+    t_start = time.perf_counter()
+    with ctx, ThreadPoolExecutor(cores) as ex:
+        i = 0
+        while i < len(tasks) and time.perf_counter() - t_start < seconds:
+            batch = tasks[i:i + cores]
+            pairs += sum(ex.map(run, batch))
+            done_rows += block * len(batch)
+            i += len(batch)
+    el = time.perf_counter() - t_start
+    flops = 4.0 * w.D * pairs
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_rows} query rows of rank share ({block}-row blocks, random heads "
+                      f"and positions, seed 0), fp64 numpy, {el:.1f} s, BLAS 1 thread/worker",
+            "seconds": round(el, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="128k")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (virtual ranks on one device); --gpus {args.gpus} "
+              "is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sequence_attention_cpa_amd as cpa
+    from sequence_attention_cpa_amd.pipeline import SharePipeline
+    from sequence_attention_cpa_amd.workloads import WORKLOADS, make_inputs
+
+    cpa.load()
+    dev = "cuda:0"
+    w = WORKLOADS[args.workload]
+    rank = args.rank
+    Qh, Kh, Vh, _ = make_inputs(w)
+    Q, K, V = Qh.to(dev), Kh.to(dev), Vh.to(dev)
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, dev, rank, rank + 1)
+    pos = pipe.pos_host.numpy()
+    if w.causal:
+        pairs = [causal_pairs(pos[rank], pos[j]) for j in range(w.N)]
+    else:
+        pairs = [w.Lr * w.Lr] * w.N
+    useful = 4.0 * w.D * w.B * w.H * sum(pairs)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pipe.step(Q, K, V)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        pipe.step(Q, K, V)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    ms_step_ev = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-kernel timing on the same stream: the ring's partials (same kernel,
+    # same arguments as inside the rank's ring), its merges, and the permutes.
+    Lr = w.Lr
+    tO = torch.empty((w.B, w.H, Lr, w.D), dtype=torch.float32, device=dev)
+    tl = torch.empty((w.B, w.H, Lr), dtype=torch.float32, device=dev)
+    pos_d = pipe.pos
+    reps = max(1, args.steps // 2)
+    evs = []
+    for _ in range(reps):
+        for s in range(w.N):
+            j = (rank + s) % w.N
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cpa.partial(pipe.Qr[0], pipe.Kr[j], pipe.Vr[j], pos_d[rank], pos_d[j], w.causal,
+                        out=tO, lse=tl)
+            b.record(stream)
+            evs.append((j, a, b))
+    mevs, pevs = [], []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cpa.merge(pipe.Or[0], pipe.lser[0], tO, tl)
+        b.record(stream)
+        mevs.append((a, b))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr)
+        b.record(stream)
+        pevs.append((a, b))
+    torch.cuda.synchronize()
+    p_ms = np.array([a.elapsed_time(b) for _, a, b in evs])
+    p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _, _ in evs])
+    p_avg_ms = float(p_ms.mean())
+    achieved = float(p_flops.mean() / (p_avg_ms * 1e-3) / 1e12)
+    m_ms = float(np.mean([a.elapsed_time(b) for a, b in mevs]))
+    m_bytes = w.B * w.H * Lr * (w.D + 1) * 4 * 3  # read acc + new, write acc (O and lse)
+    perm_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
+    perm_bytes = 2 * K.numel() * K.element_size()
+
+    value = useful / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "causal-useful attention TFLOP/s per GPU at 128k CP=4 share; % bf16 MFMA peak"
+        if args.workload == "128k" else f"causal-useful attention TFLOP/s ({args.workload} share)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} share: rank {rank} of CP={w.N} zigzag, B={w.B} H={w.H} "
+                               f"D={w.D} L={w.L}, causal={w.causal}",
+                   "B": w.B, "H": w.H, "D": w.D, "L": w.L, "N": w.N, "rank": rank,
+                   "causal": w.causal, "useful_flop_per_step": useful,
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": pmc_traffic(), "kernel": "partial_attn_mfma_kernel<128>",
+                     "avg_launch_ms": round(p_avg_ms, 4),
+                     "useful_flop_per_launch": float(p_flops.mean())},
+        "kernels": {
+            "partial_ms": [round(float(x), 4) for x in p_ms[: w.N]],
+            "merge": {"ms": round(m_ms, 4), "GB/s": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
+                      "bytes": m_bytes},
+            "permute_K": {"ms": round(perm_ms, 4),
+                          "GB/s": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
+                          "bytes": perm_bytes},
+            "ms_per_step_events": round(ms_step_ev, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu and rank == 0:
+        out["cpu_baseline"] = cpu_baseline(w, Qh, Kh, Vh, pos[rank], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * libcpattn -- context-parallel (ring) attention for one rank's share, on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: host or device pointers and
+ * sizes only; no HIP, torch or C++ types cross it (streams are void*).
+ *
+ * The method ("序列与上下文并行", section 上下文并行：注意力本身切分): the
+ * sequence is cut into segments, one per rank.  Rank i keeps its own Q
+ * segment and meets every rank's K/V segment in ring order j = i, i+1, ...
+ * (mod N); each meeting yields a partial attention result that is folded into
+ * the running result by online softmax.  Causal work is balanced by a
+ * Z-shaped (zigzag) chunk assignment, and every rank knows the global
+ * position of each of its tokens (same page, section 工程实践).  Attention
+ * itself is softmax(Q K^T / sqrt(D) + mask) V ("Tensor并行与算子拆分",
+ * section 注意力的并行化优化).  On one GPU the ranks are index ranges.
+ *
+ * Conventions shared by every call:
+ *  - Tensors are dense, row-major and contiguous.  Per-head data is
+ *    [B, H, rows, D] with D fastest; "rank-major" data is [N, B, H, L/N, D].
+ *  - Element types: cpa_dtype for Q/K/V; O and lse are always float32.
+ *  - Device pointers must be 16-byte aligned (offset tables 8-byte aligned).
+ *  - Ownership: the caller allocates and frees every buffer; the library
+ *    keeps no pointer after a call returns and never allocates device memory.
+ *  - Execution: every device call only enqueues work on `stream` (a
+ *    hipStream_t, or NULL for the default stream) and returns; nothing
+ *    synchronises.  A buffer may be reused once the stream has passed it.
+ *  - Errors: every call checks its arguments on the host before any launch
+ *    and returns a cpa_status; on failure nothing was enqueued (CPA_EHIP: the
+ *    launch itself failed) and cpa_last_error() explains.  No C++ exception
+ *    crosses this boundary.
+ *  - Thread safety: calls may be made from several host threads; the error
+ *    text is per thread.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CPA_OK = 0,
+  CPA_EINVAL = 1,       /* null pointer, bad rank index, misalignment, bad flag */
+  CPA_ESHAPE = 2,       /* sizes that do not fit the method (e.g. L % 2N != 0) */
+  CPA_EDTYPE = 3,       /* unknown element type / element size */
+  CPA_EUNSUPPORTED = 4, /* valid but not built (head_dim outside {16, 64, 128}) */
+  CPA_EHIP = 5          /* the HIP runtime reported an error while launching */
+} cpa_status;
+
+typedef enum { CPA_BF16 = 0, CPA_F32 = 1 } cpa_dtype;
+
+/*
+ * Zigzag layout (host only; no GPU needed).
+ * Z-shaped assignment of "序列与上下文并行" (上下文并行, 工程实践), read as:
+ * the L tokens form 2N chunks of C = L/(2N); rank r holds chunk r and chunk
+ * 2N-1-r, so every rank gets the same causal work (2N C^2 + C key/query
+ * pairs per head).
+ *   L    total sequence length, > 0, divisible by 2N
+ *   N    number of (virtual) ranks, >= 1
+ *   out  host int64 [N, L/N]: out[r*(L/N) + t] = global position of rank r's
+ *        t-th local token (chunk r ascending, then chunk 2N-1-r ascending).
+ * Returns CPA_ESHAPE for L <= 0 or L % 2N != 0, CPA_EINVAL for N < 1 or a
+ * null `out`.
+ */
+cpa_status cpa_zigzag_layout(int64_t L, int32_t N, int64_t *out);
+
+/*
+ * Partial attention of one ring step: Q_i against (K_j, V_j)
+ * ("序列与上下文并行", 上下文并行: each step gives a partial result for the
+ * local queries).
+ *   Q      device [B, H, Lq, D] of `dt`
+ *   K, V   device [B, H, Lk, D] of `dt`
+ *   q_off  device int64 [Lq], k_off device int64 [Lk]: global token
+ *          positions (precondition: strictly increasing; the kernel classifies
+ *          whole tiles from their first and last entries)
+ *   causal nonzero: key u is visible to query t iff k_off[u] <= q_off[t]
+ *   scale  score scale; <= 0 selects 1/sqrt(D)
+ *   O      device float32 [B, H, Lq, D]  (written)
+ *   lse    device float32 [B, H, Lq]     (written): natural-log sum of
+ *          exp(scaled scores) over the visible keys
+ * A query with no visible key gets O = 0 and lse = -inf.  D must be 16, 64 or
+ * 128 (CPA_EUNSUPPORTED otherwise).  bf16 inputs are multiplied on the
+ * matrix cores with float32 accumulation; softmax is float32.
+ */
+cpa_status cpa_partial(const void *Q, const void *K, const void *V, cpa_dtype dt,
+                       int32_t B, int32_t H, int64_t Lq, int64_t Lk, int32_t D,
+                       const int64_t *q_off, const int64_t *k_off, int32_t causal,
+                       float scale, float *O, float *lse, void *stream);
+
+/*
+ * Online-softmax merge, in place ("序列与上下文并行", 上下文并行: partial
+ * results are folded together incrementally by online softmax):
+ *   lse = ln(e^lse_acc + e^lse_new),
+ *   O   = O_acc e^(lse_acc - lse) + O_new e^(lse_new - lse).
+ * An empty side (lse = -inf) has weight 0; two empty sides give (0, -inf).
+ *   O_acc, lse_acc  device float32 [rows, D] / [rows], read and written
+ *   O_new, lse_new  device float32 [rows, D] / [rows], read only
+ *   rows            number of query rows (B*H*Lq), >= 0; D in {16, 64, 128}
+ */
+cpa_status cpa_merge(float *O_acc, float *lse_acc, const float *O_new,
+                     const float *lse_new, int64_t rows, int32_t D, void *stream);
+
+/*
+ * Workspace bytes cpa_rank_forward needs: one partial (O, lse) in float32,
+ * B*H*(L/N)*(D+1)*4 bytes rounded up to 256.  Returns 0 for invalid sizes.
+ */
+size_t cpa_rank_forward_workspace(int32_t B, int32_t H, int64_t L, int32_t N, int32_t D);
+
+/*
+ * Whole ring for virtual rank i ("序列与上下文并行", 上下文并行): for
+ * s = 0 .. N-1, j = (i + s) mod N, the partial of Q_i against (K_j, V_j);
+ * step 0 writes (O_i, lse_i) directly, later steps go to the workspace and
+ * are merged in.  Enqueues N partials and N-1 merges on `stream`.
+ *   i, N          rank index 0 <= i < N
+ *   Q_i           device [B, H, L/N, D] of `dt` (rank i's tokens, rank order)
+ *   K_all, V_all  device rank-major [N, B, H, L/N, D] of `dt`
+ *   pos_all       device int64 [N, L/N], e.g. cpa_zigzag_layout's table
+ *   O_i, lse_i    device float32 [B, H, L/N, D] / [B, H, L/N] (written)
+ *   ws, ws_bytes  device workspace of at least cpa_rank_forward_workspace()
+ *                 bytes (CPA_EINVAL if smaller); unused when N == 1
+ */
+cpa_status cpa_rank_forward(int32_t i, int32_t N, const void *Q_i, const void *K_all,
+                            const void *V_all, const int64_t *pos_all, cpa_dtype dt,
+                            int32_t B, int32_t H, int64_t L, int32_t D, int32_t causal,
+                            float scale, float *O_i, float *lse_i, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * Permutation between global order and rank-major zigzag order, for ranks
+ * [rank_lo, rank_hi) (the data-pipeline step of "序列与上下文并行", 工程实践:
+ * each rank's data must follow the CP layout).
+ *   forward (inverse == 0): dst[r - rank_lo, b, h, t, :] = src[b, h, pos_all[r, t], :]
+ *   inverse (inverse != 0): dst[b, h, pos_all[r, t], :] = src[r - rank_lo, b, h, t, :]
+ *   src, dst     device, elements of `elem_bytes` (2, 4 or 8); row = D elements
+ *   B, H, L, D   global shape [B, H, L, D]; D >= 1 (D = 1 for lse)
+ *   pos_all      device int64 [N, L/N]; every entry in [0, L)
+ *   rank_lo/hi   0 <= rank_lo < rank_hi <= N
+ * Rows of dst not named by the selected ranks are left untouched (inverse).
+ * A pure copy: bit-exact.  Row bytes D*elem_bytes must be a multiple of 4.
+ */
+cpa_status cpa_zigzag_permute(const void *src, void *dst, int32_t elem_bytes,
+                              int32_t B, int32_t H, int64_t L, int32_t D,
+                              const int64_t *pos_all, int32_t N, int32_t rank_lo,
+                              int32_t rank_hi, int32_t inverse, void *stream);
+
+/* Text of the last error on the calling thread ("" if none); valid until the
+ * thread's next call into the library. */
+const char *cpa_last_error(void);
+
+/* Library version, e.g. "libcpattn 0.1.0 gfx950". */
+const char *cpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,1 +1,139 @@
-"""libcpattn: context-parallel ring attention on MI355X (gfx950)."""
+"""libcpattn: context-parallel ring attention on MI355X (gfx950).
+
+Python names mirror the C ABI (include/cpattn.h) without the `cpa_` prefix.
+Tensors supply device memory; the HIP stream is torch's current stream on the
+tensors' device.  Nothing is computed here: every call goes to the library.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import (CPA_BF16, CPA_F32, CpaError, check, last_error, load,  # noqa: F401
+                   version)
+
+__all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
+           "zigzag_permute", "last_error", "version", "CpaError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return CPA_BF16
+    if t.dtype == torch.float32:
+        return CPA_F32
+    raise CpaError(3, f"unsupported tensor dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise CpaError(1, "tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise CpaError(1, "tensors must be contiguous")
+
+
+def zigzag_layout(L: int, N: int):
+    """int64 CPU tensor [N, L/N] of global token positions per rank (host call)."""
+    torch = _torch()
+    if N < 1 or L <= 0 or L % (2 * N):
+        out = torch.empty(1, dtype=torch.int64)
+    else:
+        out = torch.empty((N, L // N), dtype=torch.int64)
+    check(load().cpa_zigzag_layout(L, N, ctypes.cast(out.data_ptr(), ctypes.POINTER(ctypes.c_int64))))
+    return out
+
+
+def partial(Q, K, V, q_off, k_off, causal: bool, scale: float = 0.0, out=None, lse=None):
+    """(O, lse) of Q [B,H,Lq,D] against K/V [B,H,Lk,D] with global positions."""
+    torch = _torch()
+    B, H, Lq, D = Q.shape
+    Lk = K.shape[2]
+    if out is None:
+        out = torch.empty((B, H, Lq, D), dtype=torch.float32, device=Q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=Q.device)
+    _need_gpu(Q, K, V, q_off, k_off, out, lse)
+    check(load().cpa_partial(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, Lq, Lk, D,
+                             _ptr(q_off), _ptr(k_off), int(bool(causal)), float(scale),
+                             _ptr(out), _ptr(lse), _stream(Q)))
+    return out, lse
+
+
+def merge(O_acc, lse_acc, O_new, lse_new):
+    """In-place online-softmax merge of (O_new, lse_new) into (O_acc, lse_acc)."""
+    _need_gpu(O_acc, lse_acc, O_new, lse_new)
+    D = O_acc.shape[-1]
+    rows = O_acc.numel() // D
+    check(load().cpa_merge(_ptr(O_acc), _ptr(lse_acc), _ptr(O_new), _ptr(lse_new), rows, D,
+                           _stream(O_acc)))
+    return O_acc, lse_acc
+
+
+def rank_forward_workspace(B: int, H: int, L: int, N: int, D: int) -> int:
+    return int(load().cpa_rank_forward_workspace(B, H, L, N, D))
+
+
+def rank_forward(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool, scale: float = 0.0,
+                 out=None, lse=None, workspace=None):
+    """Rank i's ring: Q_i [B,H,L/N,D] vs rank-major K_all/V_all [N,B,H,L/N,D]."""
+    torch = _torch()
+    B, H, Lr, D = Q_i.shape
+    L = Lr * N
+    if out is None:
+        out = torch.empty((B, H, Lr, D), dtype=torch.float32, device=Q_i.device)
+    if lse is None:
+        lse = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
+    ws_bytes = rank_forward_workspace(B, H, L, N, D)
+    if workspace is None and N > 1:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=Q_i.device)
+    _need_gpu(Q_i, K_all, V_all, pos_all, out, lse, workspace)
+    check(load().cpa_rank_forward(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
+                                  _dtype_code(Q_i), B, H, L, D, int(bool(causal)), float(scale),
+                                  _ptr(out), _ptr(lse), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _stream(Q_i)))
+    return out, lse
+
+
+def zigzag_permute(src, pos_all, N: int, inverse: bool = False, rank_lo: int = 0,
+                   rank_hi: int | None = None, out=None):
+    """Global [B,H,L,D] -> rank-major [nr,B,H,L/N,D] (or back with inverse=True)
+    for ranks [rank_lo, rank_hi).  A 3-D source/target [B,H,L] is treated as D=1."""
+    torch = _torch()
+    rank_hi = N if rank_hi is None else rank_hi
+    nr = rank_hi - rank_lo
+    if inverse:
+        squeeze = src.dim() == 4  # [nr,B,H,Lr] for lse
+        x = src.unsqueeze(-1) if squeeze else src
+        _, B, H, Lr, D = x.shape
+        L = Lr * N
+        if out is None:
+            out = torch.zeros((B, H, L) if squeeze else (B, H, L, D), dtype=src.dtype, device=src.device)
+    else:
+        squeeze = src.dim() == 3
+        x = src.unsqueeze(-1) if squeeze else src
+        B, H, L, D = x.shape
+        Lr = L // N
+        if out is None:
+            shape = (nr, B, H, Lr) if squeeze else (nr, B, H, Lr, D)
+            out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    _need_gpu(src, pos_all, out)
+    check(load().cpa_zigzag_permute(_ptr(src), _ptr(out), src.element_size(), B, H, L, D,
+                                    _ptr(pos_all), N, rank_lo, rank_hi, int(bool(inverse)),
+                                    _stream(src)))
+    return out

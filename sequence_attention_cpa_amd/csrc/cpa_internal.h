@@ -1,0 +1,33 @@
+// Internal launch interface between the C-ABI host layer (cpattn.cpp) and the
+// HIP kernels.  Arguments are already validated by the caller; each launcher
+// enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace cpa {
+
+// Partial attention, bf16 inputs on the matrix cores (D = 64 or 128).
+hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V,
+                               const int64_t* q_off, const int64_t* k_off, float* O,
+                               float* lse, int BH, int64_t Lq, int64_t Lk, int D, bool causal,
+                               float scale, hipStream_t stream);
+
+// Partial attention, one query row per thread, fp32 arithmetic throughout
+// (fp32 inputs, and bf16 inputs with D = 16).
+hipError_t launch_partial_rowwise(const void* Q, const void* K, const void* V, bool bf16,
+                                  const int64_t* q_off, const int64_t* k_off, float* O,
+                                  float* lse, int BH, int64_t Lq, int64_t Lk, int D, bool causal,
+                                  float scale, hipStream_t stream);
+
+// In-place online-softmax merge of `rows` rows of D floats.
+hipError_t launch_merge(float* O_acc, float* lse_acc, const float* O_new, const float* lse_new,
+                        int64_t rows, int D, hipStream_t stream);
+
+// Row gather/scatter between [BH, L, row_bytes] and rank-major [nr, BH, L/N, row_bytes].
+hipError_t launch_permute(const void* src, void* dst, int64_t row_bytes, int64_t BH, int64_t L,
+                          const int64_t* pos_all, int N, int rank_lo, int rank_hi, bool inverse,
+                          hipStream_t stream);
+
+}  // namespace cpa

@@ -1,0 +1,216 @@
+// C-ABI layer of libcpattn: argument checks, the zigzag layout, and the ring
+// driver that strings partial-attention and merge launches together.  Every
+// check runs on the host before anything is enqueued; errors are returned as
+// cpa_status with a per-thread message.  No exception leaves this file.
+#include "../../include/cpattn.h"
+#include "cpa_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_err;
+
+cpa_status fail(cpa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+cpa_status ok() {
+  g_err.clear();
+  return CPA_OK;
+}
+
+cpa_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CPA_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool supported_d(int32_t D) { return D == 16 || D == 64 || D == 128; }
+
+cpa_status check_partial(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
+                         int32_t H, int64_t Lq, int64_t Lk, int32_t D, const int64_t* q_off,
+                         const int64_t* k_off, int32_t causal, const float* O, const float* lse) {
+  if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
+  if (B < 1 || H < 1) return fail(CPA_ESHAPE, "B and H must be >= 1 (B=%d, H=%d)", B, H);
+  if (Lq < 0 || Lk < 0) return fail(CPA_ESHAPE, "Lq and Lk must be >= 0 (Lq=%lld, Lk=%lld)",
+                                    (long long)Lq, (long long)Lk);
+  if (Lq > (int64_t)1 << 30 || Lk > (int64_t)1 << 30)
+    return fail(CPA_ESHAPE, "Lq and Lk are limited to 2^30 rows");
+  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if (!supported_d(D)) return fail(CPA_EUNSUPPORTED, "head_dim %d not built (16, 64, 128)", D);
+  if (Lq > 0 && (!Q || !O || !lse)) return fail(CPA_EINVAL, "null Q/O/lse pointer");
+  if (Lq > 0 && Lk > 0 && (!K || !V)) return fail(CPA_EINVAL, "null K/V pointer");
+  if (causal && Lq > 0 && Lk > 0 && (!q_off || !k_off))
+    return fail(CPA_EINVAL, "causal attention needs q_off and k_off");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(CPA_EINVAL, "Q, K, V and O must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(q_off, 8) || !aligned(k_off, 8))
+    return fail(CPA_EINVAL, "lse must be 4-byte and offsets 8-byte aligned");
+  return CPA_OK;
+}
+
+cpa_status enqueue_partial(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
+                           int32_t H, int64_t Lq, int64_t Lk, int32_t D, const int64_t* q_off,
+                           const int64_t* k_off, int32_t causal, float scale, float* O, float* lse,
+                           hipStream_t st) {
+  if (Lq == 0) return ok();
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
+  const int BH = B * H;
+  hipError_t e;
+  if (Lk == 0) {
+    // No keys at all: every row is empty.  The row-wise kernel writes (0, -inf)
+    // without touching K/V.
+    e = cpa::launch_partial_rowwise(Q, K, V, dt == CPA_BF16, q_off, k_off, O, lse, BH, Lq, 0, D,
+                                    false, scale, st);
+  } else if (dt == CPA_BF16 && (D == 64 || D == 128)) {
+    e = cpa::launch_partial_mfma(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, D, causal != 0, scale,
+                                 st);
+  } else {
+    e = cpa::launch_partial_rowwise(Q, K, V, dt == CPA_BF16, q_off, k_off, O, lse, BH, Lq, Lk, D,
+                                    causal != 0, scale, st);
+  }
+  return from_hip(e, "partial attention launch");
+}
+
+cpa_status check_rank_shape(int32_t N, int64_t L, int32_t B, int32_t H, int32_t D) {
+  if (N < 1) return fail(CPA_EINVAL, "N must be >= 1 (N=%d)", N);
+  if (L <= 0 || L % (2 * (int64_t)N) != 0)
+    return fail(CPA_ESHAPE, "L must be > 0 and divisible by 2N (L=%lld, N=%d)", (long long)L, N);
+  if (B < 1 || H < 1) return fail(CPA_ESHAPE, "B and H must be >= 1");
+  if (D < 1) return fail(CPA_ESHAPE, "D must be >= 1");
+  return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cpa_last_error(void) { return g_err.c_str(); }
+
+const char* cpa_version(void) { return "libcpattn 0.1.0 gfx950"; }
+
+cpa_status cpa_zigzag_layout(int64_t L, int32_t N, int64_t* out) {
+  if (N < 1) return fail(CPA_EINVAL, "N must be >= 1 (N=%d)", N);
+  if (L <= 0 || L % (2 * (int64_t)N) != 0)
+    return fail(CPA_ESHAPE, "L must be > 0 and divisible by 2N (L=%lld, N=%d)", (long long)L, N);
+  if (!out) return fail(CPA_EINVAL, "null output table");
+  const int64_t C = L / (2 * (int64_t)N);
+  const int64_t Lr = 2 * C;
+  for (int64_t r = 0; r < N; ++r) {
+    const int64_t early = r * C;                        // chunk r
+    const int64_t late = (2 * (int64_t)N - 1 - r) * C;  // chunk 2N-1-r
+    int64_t* row = out + r * Lr;
+    for (int64_t t = 0; t < C; ++t) {
+      row[t] = early + t;
+      row[C + t] = late + t;
+    }
+  }
+  return ok();
+}
+
+cpa_status cpa_partial(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
+                       int32_t H, int64_t Lq, int64_t Lk, int32_t D, const int64_t* q_off,
+                       const int64_t* k_off, int32_t causal, float scale, float* O, float* lse,
+                       void* stream) {
+  cpa_status st = check_partial(Q, K, V, dt, B, H, Lq, Lk, D, q_off, k_off, causal, O, lse);
+  if (st != CPA_OK) return st;
+  return enqueue_partial(Q, K, V, dt, B, H, Lq, Lk, D, q_off, k_off, causal, scale, O, lse,
+                         (hipStream_t)stream);
+}
+
+cpa_status cpa_merge(float* O_acc, float* lse_acc, const float* O_new, const float* lse_new,
+                     int64_t rows, int32_t D, void* stream) {
+  if (rows < 0) return fail(CPA_ESHAPE, "rows must be >= 0");
+  if (!supported_d(D)) return fail(CPA_EUNSUPPORTED, "head_dim %d not built (16, 64, 128)", D);
+  if (rows == 0) return ok();
+  if (!O_acc || !lse_acc || !O_new || !lse_new) return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(O_acc, 16) || !aligned(O_new, 16)) return fail(CPA_EINVAL, "O must be 16-byte aligned");
+  if (!aligned(lse_acc, 4) || !aligned(lse_new, 4)) return fail(CPA_EINVAL, "lse must be 4-byte aligned");
+  return from_hip(cpa::launch_merge(O_acc, lse_acc, O_new, lse_new, rows, D, (hipStream_t)stream),
+                  "merge launch");
+}
+
+size_t cpa_rank_forward_workspace(int32_t B, int32_t H, int64_t L, int32_t N, int32_t D) {
+  if (N < 1 || B < 1 || H < 1 || D < 1 || L <= 0 || L % (2 * (int64_t)N) != 0) return 0;
+  const size_t rows = (size_t)B * H * (size_t)(L / N);
+  const size_t o_bytes = (rows * D * 4 + 255) / 256 * 256;
+  const size_t l_bytes = (rows * 4 + 255) / 256 * 256;
+  return o_bytes + l_bytes;
+}
+
+cpa_status cpa_rank_forward(int32_t i, int32_t N, const void* Q_i, const void* K_all,
+                            const void* V_all, const int64_t* pos_all, cpa_dtype dt, int32_t B,
+                            int32_t H, int64_t L, int32_t D, int32_t causal, float scale,
+                            float* O_i, float* lse_i, void* ws, size_t ws_bytes, void* stream) {
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (i < 0 || i >= N) return fail(CPA_EINVAL, "rank index %d outside [0, %d)", i, N);
+  if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
+  const int64_t Lr = L / N;
+  st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, O_i, lse_i);
+  if (st != CPA_OK) return st;
+  const size_t need = cpa_rank_forward_workspace(B, H, L, N, D);
+  if (N > 1) {
+    if (!ws) return fail(CPA_EINVAL, "null workspace");
+    if (ws_bytes < need)
+      return fail(CPA_EINVAL, "workspace too small: %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(CPA_EINVAL, "workspace must be 256-byte aligned");
+  }
+  const size_t esz = dt == CPA_BF16 ? 2 : 4;
+  const size_t rank_elems = (size_t)B * H * Lr * D;
+  const size_t rows = (size_t)B * H * Lr;
+  float* tO = (float*)ws;
+  float* tl = (float*)((char*)ws + (rows * D * 4 + 255) / 256 * 256);
+  hipStream_t hs = (hipStream_t)stream;
+  const int64_t* q_off = pos_all + (int64_t)i * Lr;
+  for (int32_t s = 0; s < N; ++s) {
+    const int32_t j = (i + s) % N;  // ring order: own block first, then i+1, i+2, ...
+    const char* Kj = (const char*)K_all + (size_t)j * rank_elems * esz;
+    const char* Vj = (const char*)V_all + (size_t)j * rank_elems * esz;
+    const int64_t* k_off = pos_all + (int64_t)j * Lr;
+    if (s == 0) {
+      st = enqueue_partial(Q_i, Kj, Vj, dt, B, H, Lr, Lr, D, q_off, k_off, causal, scale, O_i,
+                           lse_i, hs);
+      if (st != CPA_OK) return st;
+    } else {
+      st = enqueue_partial(Q_i, Kj, Vj, dt, B, H, Lr, Lr, D, q_off, k_off, causal, scale, tO, tl,
+                           hs);
+      if (st != CPA_OK) return st;
+      st = from_hip(cpa::launch_merge(O_i, lse_i, tO, tl, (int64_t)rows, D, hs), "merge launch");
+      if (st != CPA_OK) return st;
+    }
+  }
+  return ok();
+}
+
+cpa_status cpa_zigzag_permute(const void* src, void* dst, int32_t elem_bytes, int32_t B,
+                              int32_t H, int64_t L, int32_t D, const int64_t* pos_all, int32_t N,
+                              int32_t rank_lo, int32_t rank_hi, int32_t inverse, void* stream) {
+  if (elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return fail(CPA_EDTYPE, "elem_bytes must be 2, 4 or 8 (got %d)", elem_bytes);
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (rank_lo < 0 || rank_hi > N || rank_lo >= rank_hi)
+    return fail(CPA_EINVAL, "rank range [%d, %d) invalid for N=%d", rank_lo, rank_hi, N);
+  const int64_t row_bytes = (int64_t)D * elem_bytes;
+  if (row_bytes % 4 != 0) return fail(CPA_ESHAPE, "row bytes D*elem_bytes must be a multiple of 4");
+  if (!src || !dst || !pos_all) return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(CPA_EINVAL, "src/dst must be 16-byte aligned");
+  if (!aligned(pos_all, 8)) return fail(CPA_EINVAL, "pos_all must be 8-byte aligned");
+  return from_hip(cpa::launch_permute(src, dst, row_bytes, (int64_t)B * H, L, pos_all, N, rank_lo,
+                                      rank_hi, inverse != 0, (hipStream_t)stream),
+                  "permute launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+"""One pass of the hot path for a set of virtual ranks, built from library calls.
+
+For ranks [rank_lo, rank_hi) of an N-way zigzag split of a [B, H, L, D]
+sequence: permute K and V into rank-major order (every rank's K/V is needed by
+the ring), permute the ranks' Q, run each rank's ring (N partials, N-1
+merges), and scatter the ranks' O and lse back to global token order.  On one
+GPU the other ranks' K/V shares are slices of the same buffers, so the ring
+needs no communication.
+
+All buffers are allocated once in the constructor; `step` allocates nothing.
+"""
+from __future__ import annotations
+
+from . import rank_forward, rank_forward_workspace, zigzag_layout, zigzag_permute
+
+
+class SharePipeline:
+    def __init__(self, B: int, H: int, L: int, D: int, N: int, causal: bool, dtype, device,
+                 rank_lo: int = 0, rank_hi: int | None = None, scale: float = 0.0):
+        import torch
+
+        self.B, self.H, self.L, self.D, self.N = B, H, L, D, N
+        self.causal, self.scale = causal, scale
+        self.rank_lo = rank_lo
+        self.rank_hi = N if rank_hi is None else rank_hi
+        nr = self.rank_hi - self.rank_lo
+        Lr = L // N
+        self.pos_host = zigzag_layout(L, N)
+        self.pos = self.pos_host.to(device)
+        self.Kr = torch.empty((N, B, H, Lr, D), dtype=dtype, device=device)
+        self.Vr = torch.empty_like(self.Kr)
+        self.Qr = torch.empty((nr, B, H, Lr, D), dtype=dtype, device=device)
+        self.Or = torch.empty((nr, B, H, Lr, D), dtype=torch.float32, device=device)
+        self.lser = torch.empty((nr, B, H, Lr), dtype=torch.float32, device=device)
+        self.ws = torch.empty(max(rank_forward_workspace(B, H, L, N, D), 1), dtype=torch.uint8,
+                              device=device)
+        self.O = torch.zeros((B, H, L, D), dtype=torch.float32, device=device)
+        self.lse = torch.full((B, H, L), float("-inf"), dtype=torch.float32, device=device)
+
+    def step(self, Q, K, V):
+        """Q, K, V: global [B, H, L, D] on the device.  Returns global (O, lse);
+        rows of ranks outside [rank_lo, rank_hi) are left as initialised."""
+        N, lo, hi = self.N, self.rank_lo, self.rank_hi
+        zigzag_permute(K, self.pos, N, out=self.Kr)
+        zigzag_permute(V, self.pos, N, out=self.Vr)
+        zigzag_permute(Q, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Qr)
+        self.ring()
+        zigzag_permute(self.Or, self.pos, N, inverse=True, rank_lo=lo, rank_hi=hi, out=self.O)
+        zigzag_permute(self.lser, self.pos, N, inverse=True, rank_lo=lo, rank_hi=hi, out=self.lse)
+        return self.O, self.lse
+
+    def ring(self):
+        """The ring part only (inputs already rank-major)."""
+        for k, i in enumerate(range(self.rank_lo, self.rank_hi)):
+            rank_forward(i, self.N, self.Qr[k], self.Kr, self.Vr, self.pos, self.causal,
+                         self.scale, out=self.Or[k], lse=self.lser[k], workspace=self.ws)

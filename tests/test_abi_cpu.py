@@ -1,0 +1,198 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, computes the zigzag layout bit-exactly, and rejects bad arguments
+on the host before any launch (so these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+from oracle import cpa_oracle
+
+import sequence_attention_cpa_amd as cpa
+from sequence_attention_cpa_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+def header_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libcpattn.so is not built (python -m sequence_attention_cpa_amd.build)")
+    return _lib.load()
+
+
+def test_exports_every_header_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert cpa.version().startswith("libcpattn")
+
+
+def test_header_is_plain_c(tmp_path):
+    """The header compiles as C99 and links against the library from C."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    prog = tmp_path / "t.c"
+    prog.write_text(
+        '#include "cpattn.h"\n#include <stdio.h>\n'
+        "int main(void){ int64_t out[64]; cpa_status s = cpa_zigzag_layout(64, 4, out);\n"
+        ' printf("%d %lld %lld\\n", (int)s, (long long)out[8], (long long)out[16]);\n'
+        " return s == CPA_OK && out[8] == 56 && out[16] == 8 ? 0 : 1; }\n")
+    exe = tmp_path / "t"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(prog), "-o", str(exe), _lib.LIB_PATH,
+                        f"-Wl,-rpath,{os.path.dirname(_lib.LIB_PATH)}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("L,N", [(64, 4), (128, 4), (12288, 4), (131072, 4), (1048576, 8),
+                                 (2, 1), (96, 3), (40, 5)])
+def test_layout_matches_oracle_bit_exact(lib, L, N):
+    got = cpa.zigzag_layout(L, N).numpy()
+    assert got.dtype == np.int64
+    assert np.array_equal(got, cpa_oracle.zigzag_layout(L, N))
+
+
+def test_layout_errors(lib):
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.zigzag_layout(63, 4)
+    assert e.value.status == _lib.CPA_ESHAPE and "2N" in str(e.value)
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.zigzag_layout(64, 0)
+    assert e.value.status == _lib.CPA_EINVAL
+    assert lib.cpa_zigzag_layout(64, 4, None) == _lib.CPA_EINVAL
+    out = (ctypes.c_int64 * 64)()
+    assert lib.cpa_zigzag_layout(64, 4, out) == _lib.CPA_OK
+    assert cpa.last_error() == ""
+
+
+# Fake but aligned device addresses: validation must reject before using them.
+P = 0x100000
+
+
+def _partial(lib, **kw):
+    a = dict(Q=P, K=P, V=P, dt=_lib.CPA_BF16, B=1, H=2, Lq=64, Lk=64, D=128, q_off=P, k_off=P,
+             causal=1, scale=0.0, O=P, lse=P, stream=None)
+    a.update(kw)
+    return lib.cpa_partial(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["H"], a["Lq"], a["Lk"],
+                           a["D"], a["q_off"], a["k_off"], a["causal"], a["scale"], a["O"],
+                           a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), _lib.CPA_EDTYPE),
+    (dict(D=32), _lib.CPA_EUNSUPPORTED),
+    (dict(D=256), _lib.CPA_EUNSUPPORTED),
+    (dict(B=0), _lib.CPA_ESHAPE),
+    (dict(H=-1), _lib.CPA_ESHAPE),
+    (dict(Lq=-1), _lib.CPA_ESHAPE),
+    (dict(Lk=(1 << 30) + 1), _lib.CPA_ESHAPE),
+    (dict(Q=None), _lib.CPA_EINVAL),
+    (dict(V=None), _lib.CPA_EINVAL),
+    (dict(lse=None), _lib.CPA_EINVAL),
+    (dict(q_off=None), _lib.CPA_EINVAL),
+    (dict(K=P + 8), _lib.CPA_EINVAL),
+    (dict(O=P + 4), _lib.CPA_EINVAL),
+    (dict(k_off=P + 4), _lib.CPA_EINVAL),
+])
+def test_partial_rejects(lib, kw, status):
+    assert _partial(lib, **kw) == status
+    assert cpa.last_error() != ""
+
+
+def test_partial_empty_query_block_is_a_no_op(lib):
+    """Lq = 0 is valid and enqueues nothing (so it needs no GPU)."""
+    assert _partial(lib, Lq=0) == _lib.CPA_OK
+    assert _partial(lib, Lq=0, Q=None, O=None, lse=None) == _lib.CPA_OK
+
+
+def test_merge_rejects(lib):
+    assert lib.cpa_merge(P, P, P, P, -1, 128, None) == _lib.CPA_ESHAPE
+    assert lib.cpa_merge(P, P, P, P, 10, 8, None) == _lib.CPA_EUNSUPPORTED
+    assert lib.cpa_merge(None, P, P, P, 10, 128, None) == _lib.CPA_EINVAL
+    assert lib.cpa_merge(P + 4, P, P, P, 10, 128, None) == _lib.CPA_EINVAL
+    assert lib.cpa_merge(P, P + 2, P, P, 10, 128, None) == _lib.CPA_EINVAL
+    assert lib.cpa_merge(None, None, None, None, 0, 128, None) == _lib.CPA_OK
+
+
+def test_workspace_size(lib):
+    B, H, L, N, D = 1, 4, 131072, 4, 128
+    rows = B * H * (L // N)
+    want = -(-rows * D * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert cpa.rank_forward_workspace(B, H, L, N, D) == want == 64 * 2**20 + 512 * 2**10
+    assert cpa.rank_forward_workspace(1, 1, 63, 4, 16) == 0
+    assert cpa.rank_forward_workspace(1, 1, 64, 0, 16) == 0
+
+
+def _rank(lib, **kw):
+    a = dict(i=0, N=4, Q=P, K=P, V=P, pos=P, dt=_lib.CPA_BF16, B=1, H=2, L=256, D=128, causal=1,
+             scale=0.0, O=P, lse=P, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.cpa_rank_forward(a["i"], a["N"], a["Q"], a["K"], a["V"], a["pos"], a["dt"], a["B"],
+                                a["H"], a["L"], a["D"], a["causal"], a["scale"], a["O"], a["lse"],
+                                a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(i=4), _lib.CPA_EINVAL),
+    (dict(i=-1), _lib.CPA_EINVAL),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(L=260), _lib.CPA_ESHAPE),
+    (dict(D=48), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=2), _lib.CPA_EDTYPE),
+    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(ws=None), _lib.CPA_EINVAL),
+    (dict(ws_bytes=1000), _lib.CPA_EINVAL),
+    (dict(ws=P + 16), _lib.CPA_EINVAL),
+    (dict(Q=P + 2), _lib.CPA_EINVAL),
+])
+def test_rank_forward_rejects(lib, kw, status):
+    assert _rank(lib, **kw) == status
+    assert cpa.last_error() != ""
+
+
+def _perm(lib, **kw):
+    a = dict(src=P, dst=P, eb=2, B=1, H=2, L=256, D=128, pos=P, N=4, lo=0, hi=4, inv=0, stream=None)
+    a.update(kw)
+    return lib.cpa_zigzag_permute(a["src"], a["dst"], a["eb"], a["B"], a["H"], a["L"], a["D"],
+                                  a["pos"], a["N"], a["lo"], a["hi"], a["inv"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(eb=3), _lib.CPA_EDTYPE),
+    (dict(L=250), _lib.CPA_ESHAPE),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(lo=2, hi=2), _lib.CPA_EINVAL),
+    (dict(hi=5), _lib.CPA_EINVAL),
+    (dict(lo=-1), _lib.CPA_EINVAL),
+    (dict(D=1, eb=2), _lib.CPA_ESHAPE),
+    (dict(src=None), _lib.CPA_EINVAL),
+    (dict(dst=P + 8), _lib.CPA_EINVAL),
+    (dict(pos=P + 4), _lib.CPA_EINVAL),
+    (dict(D=0), _lib.CPA_ESHAPE),
+])
+def test_permute_rejects(lib, kw, status):
+    assert _perm(lib, **kw) == status
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 2, 64, 16)
+    pos = torch.zeros(64, dtype=torch.int64)
+    with pytest.raises(cpa.CpaError):
+        cpa.partial(x, x, x, pos, pos, True)

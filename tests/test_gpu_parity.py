@@ -1,0 +1,329 @@
+"""GPU parity: every call of libcpattn against the CPU fp64 oracle, through the
+C ABI (via the thin ctypes binding), on seeded synthetic inputs."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cpa_oracle
+from parity_helpers import (assert_bf16_close, assert_f32_close, oracle_rows, widen,
+                            check_empty_rows)
+
+import sequence_attention_cpa_amd as cpa
+from sequence_attention_cpa_amd.pipeline import SharePipeline
+from sequence_attention_cpa_amd.workloads import WORKLOADS, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    cpa.load()  # fails loudly if libcpattn.so is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rand(shape, dtype, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(dtype)
+
+
+def increasing_offsets(n, seed, start=0):
+    """Strictly increasing global positions with random gaps (not a zigzag)."""
+    g = np.random.default_rng(seed)
+    return start + np.cumsum(g.integers(1, 4, size=n)).astype(np.int64)
+
+
+def run_partial(Q, K, V, q_off, k_off, causal, scale=0.0):
+    O, lse = cpa.partial(Q.to(DEV), K.to(DEV), V.to(DEV), torch.from_numpy(q_off).to(DEV),
+                         torch.from_numpy(k_off).to(DEV), causal, scale)
+    torch.cuda.synchronize()
+    return O.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def oracle_partial(Q, K, V, q_off, k_off, causal, scale=None):
+    return cpa_oracle.partial(widen(Q), widen(K), widen(V), q_off, k_off, causal, scale)
+
+
+# ----------------------------------------------------------------- partial
+
+PARTIAL_CASES = [
+    # B, H, Lq, Lk, D, causal, offsets
+    (1, 2, 128, 128, 128, True, "same"),       # one tile, diagonal
+    (1, 3, 300, 300, 128, True, "same"),       # ragged: 2 full + 1 partial q tile, ragged k tile
+    (2, 2, 256, 512, 128, True, "later_k"),    # keys after queries -> mostly empty
+    (1, 2, 256, 512, 128, True, "earlier_k"),  # keys before queries -> all visible, no mask
+    (1, 2, 200, 333, 128, False, "same"),      # non-causal, ragged both ways
+    (2, 2, 192, 130, 64, True, "random"),      # D=64, random increasing offsets
+    (1, 4, 128, 64, 64, False, "same"),
+    (1, 2, 517, 259, 128, True, "random"),
+]
+
+
+def make_offsets(kind, Lq, Lk, seed):
+    if kind == "same":
+        return np.arange(Lq, dtype=np.int64), np.arange(Lk, dtype=np.int64)
+    if kind == "later_k":
+        return np.arange(Lq, dtype=np.int64), np.arange(Lq // 2, Lq // 2 + Lk, dtype=np.int64)
+    if kind == "earlier_k":
+        return np.arange(Lk, Lk + Lq, dtype=np.int64), np.arange(Lk, dtype=np.int64)
+    q = increasing_offsets(Lq, seed)
+    k = increasing_offsets(Lk, seed + 1, start=-20)
+    return q, k
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=[str(c) for c in PARTIAL_CASES])
+def test_partial_mfma_bf16(case):
+    B, H, Lq, Lk, D, causal, kind = case
+    say("partial mfma", case)
+    Q = rand((B, H, Lq, D), torch.bfloat16, 1)
+    K = rand((B, H, Lk, D), torch.bfloat16, 2)
+    V = rand((B, H, Lk, D), torch.bfloat16, 3)
+    q_off, k_off = make_offsets(kind, Lq, Lk, 4)
+    O, lse = run_partial(Q, K, V, q_off, k_off, causal)
+    Or, lser = oracle_partial(Q, K, V, q_off, k_off, causal)
+    assert_bf16_close(O, lse, Or, lser, str(case))
+
+
+def test_partial_zigzag_small_chunks_bf16():
+    """Chunks of 8 tokens (shorter than a 64-key tile): every K tile mixes
+    visible and hidden keys of several chunks, for every (i, j) pair."""
+    B, H, L, N, D = 1, 2, 256, 16, 128
+    pos = cpa_oracle.zigzag_layout(L, N)
+    Q = rand((B, H, L, D), torch.bfloat16, 5)
+    K = rand((B, H, L, D), torch.bfloat16, 6)
+    V = rand((B, H, L, D), torch.bfloat16, 7)
+    for i in (0, 5, 15):
+        for j in (0, 3, 15):
+            pi, pj = torch.from_numpy(pos[i]), torch.from_numpy(pos[j])
+            Qi = Q[:, :, pi]
+            Kj, Vj = K[:, :, pj].contiguous(), V[:, :, pj].contiguous()
+            O, lse = run_partial(Qi.contiguous(), Kj, Vj, pos[i], pos[j], True)
+            Or, lser = oracle_partial(Qi, Kj, Vj, pos[i], pos[j], True)
+            assert_bf16_close(O, lse, Or, lser, f"i={i} j={j}")
+
+
+def test_partial_fully_hidden_rows_are_zero_and_neg_inf():
+    B, H, L, N, D = 1, 2, 1024, 4, 128
+    pos = cpa_oracle.zigzag_layout(L, N)
+    C = L // (2 * N)
+    Q = rand((B, H, L // N, D), torch.bfloat16, 8)
+    K = rand((B, H, L // N, D), torch.bfloat16, 9)
+    O, lse = run_partial(Q, K, K, pos[0], pos[2], True)
+    assert np.all(O[:, :, :C] == 0) and np.all(np.isneginf(lse[:, :, :C]))
+    Or, lser = oracle_partial(Q, K, K, pos[0], pos[2], True)
+    assert_bf16_close(O, lse, Or, lser)
+
+
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_partial_f32(D, causal):
+    """fp32 inputs: fp32 arithmetic end to end, relative error <= 1e-5."""
+    B, H, Lq, Lk = 1, 2, 40, 72
+    Q = rand((B, H, Lq, D), torch.float32, 10)
+    K = rand((B, H, Lk, D), torch.float32, 11)
+    V = rand((B, H, Lk, D), torch.float32, 12)
+    q_off = np.arange(30, 30 + Lq, dtype=np.int64)
+    k_off = np.arange(Lk, dtype=np.int64)
+    O, lse = run_partial(Q, K, V, q_off, k_off, causal)
+    Or, lser = oracle_partial(Q, K, V, q_off, k_off, causal)
+    assert_f32_close(O, lse, Or, lser)
+
+
+def test_partial_bf16_d16_rowwise():
+    Q, K, V = (rand((2, 2, 50, 16), torch.bfloat16, s) for s in (13, 14, 15))
+    off = np.arange(50, dtype=np.int64)
+    O, lse = run_partial(Q, K, V, off, off, True)
+    Or, lser = oracle_partial(Q, K, V, off, off, True)
+    assert_bf16_close(O, lse, Or, lser)
+
+
+def test_partial_explicit_scale():
+    Q, K, V = (rand((1, 2, 130, 128), torch.bfloat16, s) for s in (16, 17, 18))
+    off = np.arange(130, dtype=np.int64)
+    O, lse = run_partial(Q, K, V, off, off, True, scale=0.05)
+    Or, lser = oracle_partial(Q, K, V, off, off, True, scale=0.05)
+    assert_bf16_close(O, lse, Or, lser)
+
+
+def test_partial_empty_inputs():
+    Q = rand((1, 2, 70, 128), torch.bfloat16, 19)
+    K = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16)
+    O, lse = run_partial(Q, K, K, np.arange(70, dtype=np.int64), np.zeros(0, dtype=np.int64), True)
+    assert np.all(O == 0) and np.all(np.isneginf(lse))
+    E = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    Oe, le = cpa.partial(E, E, E, torch.zeros(0, dtype=torch.int64, device=DEV),
+                         torch.zeros(0, dtype=torch.int64, device=DEV), True)
+    assert Oe.numel() == 0 and le.numel() == 0
+
+
+def test_partial_large_logits():
+    """Outlier-sized scores (|s| in the hundreds) exercise the running-max rescale."""
+    Q = rand((1, 2, 256, 128), torch.float32, 20)
+    K = rand((1, 2, 256, 128), torch.float32, 21)
+    Q[:, :, ::7] *= 8
+    K[:, :, ::5] *= 8
+    Q, K = Q.to(torch.bfloat16), K.to(torch.bfloat16)
+    V = rand((1, 2, 256, 128), torch.bfloat16, 22)
+    off = np.arange(256, dtype=np.int64)
+    O, lse = run_partial(Q, K, V, off, off, True)
+    Or, lser = oracle_partial(Q, K, V, off, off, True)
+    assert_bf16_close(O, lse, Or, lser)
+
+
+def test_partial_deterministic():
+    Q, K, V = (rand((1, 4, 640, 128), torch.bfloat16, s).to(DEV) for s in (23, 24, 25))
+    off = torch.arange(640, dtype=torch.int64, device=DEV)
+    a = [t.clone() for t in cpa.partial(Q, K, V, off, off, True)]
+    b = cpa.partial(Q, K, V, off, off, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------- merge
+
+def test_merge_vs_oracle():
+    rows, D = 3000, 128
+    g = torch.Generator().manual_seed(30)
+    Oa, Ob = torch.randn(rows, D, generator=g), torch.randn(rows, D, generator=g)
+    la, lb = torch.randn(rows, generator=g) * 20, torch.randn(rows, generator=g) * 20
+    la[::11] = float("-inf")
+    lb[::13] = float("-inf")
+    la[::77] = float("-inf")
+    lb[::77] = float("-inf")
+    Oa[::11] = 0
+    Ob[::13] = 0
+    Oa[::77] = 0
+    Ob[::77] = 0
+    Or, lr = cpa_oracle.merge(Oa.double().numpy(), la.double().numpy(), Ob.double().numpy(),
+                              lb.double().numpy())
+    Od, ld, Obd, lbd = (t.to(DEV) for t in (Oa, la, Ob, lb))
+    cpa.merge(Od, ld, Obd, lbd)
+    torch.cuda.synchronize()
+    assert_f32_close(Od.cpu().double().numpy(), ld.cpu().double().numpy(), Or, lr)
+
+
+@pytest.mark.parametrize("D", [16, 64])
+def test_merge_small_d(D):
+    g = torch.Generator().manual_seed(31)
+    Oa, Ob = torch.randn(257, D, generator=g), torch.randn(257, D, generator=g)
+    la, lb = torch.randn(257, generator=g), torch.randn(257, generator=g)
+    Or, lr = cpa_oracle.merge(Oa.double().numpy(), la.double().numpy(), Ob.double().numpy(),
+                              lb.double().numpy())
+    Od, ld = Oa.to(DEV), la.to(DEV)
+    cpa.merge(Od, ld, Ob.to(DEV), lb.to(DEV))
+    torch.cuda.synchronize()
+    assert_f32_close(Od.cpu().double().numpy(), ld.cpu().double().numpy(), Or, lr)
+
+
+# ----------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64),
+                                     (torch.float32, 1), (torch.bfloat16, 4),
+                                     (torch.float64, 3)])
+@pytest.mark.parametrize("ranks", [(0, 4), (1, 3), (3, 4)])
+def test_permute_bit_exact(dtype, D, ranks):
+    B, H, L, N = 2, 3, 192, 4
+    pos = cpa_oracle.zigzag_layout(L, N)
+    x = rand((B, H, L, D), torch.float32, 40).to(dtype)
+    lo, hi = ranks
+    src = x[..., 0] if D == 1 else x
+    pos_d = torch.from_numpy(pos).to(DEV)
+    y = cpa.zigzag_permute(src.to(DEV), pos_d, N, rank_lo=lo, rank_hi=hi)
+    want = cpa_oracle.permute_to_ranks(x.numpy() if dtype != torch.bfloat16 else x.view(torch.int16).numpy(), pos)[lo:hi]
+    got = y.cpu()
+    got = got.view(torch.int16).numpy() if dtype == torch.bfloat16 else got.numpy()
+    if D == 1:
+        want = want[..., 0]
+    assert np.array_equal(got, want)
+    back = cpa.zigzag_permute(y, pos_d, N, inverse=True, rank_lo=lo, rank_hi=hi)
+    torch.cuda.synchronize()
+    b = back.cpu()
+    rows = np.sort(pos[lo:hi].ravel())
+    assert torch.equal(b[:, :, rows], src[:, :, rows])
+    other = np.setdiff1d(np.arange(L), rows)
+    assert torch.all(b[:, :, other] == 0)
+
+
+# ------------------------------------------------------------ rank forward
+
+def stitched_all_ranks(w, Q, K, V):
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV)
+    O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
+    torch.cuda.synchronize()
+    return O.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def test_rank_forward_tiny_f32_all_ranks():
+    w = WORKLOADS["tiny"]
+    Q, K, V, _ = make_inputs(w)
+    O, lse = stitched_all_ranks(w, Q, K, V)
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), w.causal)
+    assert_f32_close(O, lse, Or, lr)
+
+
+def test_rank_forward_demo_bf16_all_ranks():
+    w = WORKLOADS["demo"]
+    Q, K, V, _ = make_inputs(w)
+    O, lse = stitched_all_ranks(w, Q, K, V)
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), w.causal)
+    assert_bf16_close(O, lse, Or, lr, "demo")
+
+
+def test_rank_forward_12k_all_ranks_every_row():
+    w = WORKLOADS["12k"]
+    say("12k: generating")
+    Q, K, V, _ = make_inputs(w)
+    say("12k: GPU")
+    O, lse = stitched_all_ranks(w, Q, K, V)
+    say("12k: oracle")
+    rows = {(b, h): np.arange(w.L) for b in range(w.B) for h in range(w.H)}
+    ref = oracle_rows(lambda b, h: widen(Q[b, h]), lambda b, h: widen(K[b, h]),
+                      lambda b, h: widen(V[b, h]), rows, w.causal)
+    Or = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
+    lr = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
+    mx, mean = assert_bf16_close(O, lse, Or, lr, "12k")
+    say(f"12k: max {mx:.3e} mean {mean:.3e}")
+
+
+def share_check(name, rank, n_rows, block):
+    w = WORKLOADS[name]
+    say(f"{name}: generating")
+    Q, K, V, outl = make_inputs(w)
+    say(f"{name}: GPU rank {rank}")
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, rank, rank + 1)
+    Od, lsed = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
+    pos = pipe.pos_host.numpy()
+    t = sample_rows(w, rank, pos[rank], n_rows // (w.B * w.H), outl)
+    g = pos[rank][t]
+    O = Od[:, :, torch.from_numpy(g).to(DEV)].cpu().double().numpy()
+    lse = lsed[:, :, torch.from_numpy(g).to(DEV)].cpu().double().numpy()
+    torch.cuda.synchronize()
+    say(f"{name}: oracle on {len(g)} rows x {w.B * w.H} heads")
+    rows = {(b, h): g for b in range(w.B) for h in range(w.H)}
+    ref = oracle_rows(lambda b, h: widen(Q[b, h]), lambda b, h: widen(K[b, h]),
+                      lambda b, h: widen(V[b, h]), rows, w.causal, block=block)
+    Or = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
+    lr = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
+    mx, mean = assert_bf16_close(O, lse, Or, lr, name)
+    say(f"{name}: max {mx:.3e} mean {mean:.3e}")
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_rank_forward_128k_share_sampled(rank):
+    share_check("128k", rank, 1024, 32)
+
+
+@pytest.mark.timeout(900)
+def test_rank_forward_1m_share_sampled():
+    share_check("1m", 0, 256, 8)
