@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -144,6 +146,15 @@ def main():
     useful = 4.0 * w.D * w.B * w.H * sum(pairs)
 
     stream = torch.cuda.current_stream()
+    if args.copy_mib:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+        # the scale between those counters and bytes actually moved.
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         pipe.step(Q, K, V)
     torch.cuda.synchronize()

@@ -2,7 +2,7 @@
 // driver that strings partial-attention and merge launches together.  Every
 // check runs on the host before anything is enqueued; errors are returned as
 // cpa_status with a per-thread message.  No exception leaves this file.
-#include "../../include/cpattn.h"
+#include "cpattn.h"
 #include "cpa_internal.h"
 
 #include <cmath>

@@ -7,55 +7,85 @@
 // (same page as the ring, section 工程实践: every rank knows its global offsets).
 //
 // Design (bf16, D = 64 or 128):
-//  * One workgroup = 4 waves = 128 query rows; each wave owns 32 rows.
+//  * One workgroup = 4 waves = 128 query rows (32 per wave); two workgroups
+//    per CU, so every SIMD runs two independent waves.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (32 keys x 16 d) is the A operand read from
 //    LDS, the wave's Q rows are the B operand held in registers for the whole
 //    kernel.  In the 32x32 accumulator layout a lane then holds 16 keys of ONE
-//    query, so the row max / row sum need only in-lane work plus one
-//    permlane32 swap between the two half-waves.
+//    query, so the row max needs only in-lane work plus one permlane32 swap
+//    between the two half-waves.
 //  * O is accumulated transposed, O^T += V^T P^T, so each lane again owns one
-//    query row and rescaling by exp2(m_old - m_new) is lane-local.  P (fp32
-//    -> bf16, round to nearest even) is the B operand straight from the score
-//    registers; V^T comes from row-major V in LDS through ds_read_b64_tr_b16.
-//  * K/V tiles of 64 keys are staged in LDS, double buffered, with a 16-byte
-//    XOR swizzle so both operand read patterns are free of bank conflicts.
+//    query row.  P (fp32 -> bf16, round to nearest even) is the B operand
+//    straight from the score registers; V^T comes from row-major V in LDS
+//    through ds_read_b64_tr_b16.
+//  * Software pipeline: iteration t issues the matrix work of PV(t-1) and
+//    QK^T(t+1) together with the exponentials of tile t in one straight-line
+//    block, so the wave's own VALU work can issue in the shadow of its MFMAs
+//    (operands are fetched three MFMAs ahead).  Only the row max of tile t+1
+//    and the rare rescale run between the matrix phases.  (Pinning the
+//    interleave with sched_group_barrier measured slower than the compiler's
+//    own schedule.)
+//  * K and V tiles of 32 keys live in two LDS buffers each.  Iteration t
+//    starts the copies of K(t+2) and V(t) straight from global memory into
+//    LDS (global_load_lds_dwordx4, no staging registers; offsets precomputed
+//    per lane, base in SGPRs) and waits for them at its end.  The copy is
+//    issued from inline asm so the compiler does not make every LDS read wait
+//    for it.  A 16-byte XOR swizzle keeps both operand read patterns free of
+//    bank conflicts; all operand addresses are per-lane constants plus
+//    immediate offsets.
+//  * Softmax rescaling is lazy and exact: the exponent reference is an integer
+//    (log2 units) raised only when a row's max grows by more than 2^8; the
+//    rescale is then a power of two, applied with ldexp to O, l and the P of
+//    the tile already computed but not yet multiplied into O.  O is divided by
+//    the sum of the packed bf16 P (v_dot2_f32_bf16), i.e. exactly the weights
+//    the PV product used, so it stays a convex combination of V rows; lse uses
+//    the fp32 sum, which the bf16 rounding of a row's dominant weight would
+//    otherwise bias by up to 2^-9.
 //  * Keys visible to a causal row form a prefix of the K block (positions
 //    increase), so the workgroup loops only over keys below the last row's
-//    bound, and only tiles that cross the first row's bound are masked per
-//    element.  Rows that see no key write O = 0, lse = -inf.
+//    bound and only tiles that cross a row's bound are masked per element.
+//    Rows that see no key write O = 0, lse = -inf.
 //  * Workgroups are issued longest-first (last query tiles first), heads
 //    fastest, so each XCD keeps working on the same heads' K/V in its L2.
 #include "cpa_internal.h"
 
 #include <cmath>
+#include <cstdint>
+#include <type_traits>
 
 namespace cpa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int BM = 128;       // query rows per workgroup
-constexpr int BN = 64;        // keys per LDS tile
-constexpr int NTHREADS = 256; // 4 waves
+constexpr int BM = 128;        // query rows per workgroup
+constexpr int BN = 32;         // keys per LDS tile
+constexpr int NKB = BN / 32;   // 32-key MFMA blocks per tile
+constexpr int NTHREADS = 256;  // 4 waves
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct Geo {
-  static constexpr int CHUNKS = D / 8;                        // 16-byte chunks per row
+  static constexpr int CHUNKS = D / 8;               // 16-byte chunks per row
   static constexpr int ROW_BYTES = D * 2;
-  static constexpr int TILE_BYTES = BN * ROW_BYTES;           // one K or V tile
-  static constexpr int LOADS = BN * CHUNKS / NTHREADS;        // chunks per thread per tile
-  static constexpr int ROWS_PER_PASS = NTHREADS / CHUNKS;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one K or V tile
+  static constexpr int KK = D / 16;                  // MFMA k-steps over d
+  static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
+  static constexpr int RPI = 1024 / ROW_BYTES;       // tile rows per 1 KB copy instruction
+  static constexpr int IPW = TILE_BYTES / 1024 / 4;  // copy instructions per wave per tile
+  static_assert(IPW >= 1, "tile smaller than one copy instruction per wave");
 };
 
-// Physical 16-byte chunk holding logical chunk c of tile row r.
+// Physical 16-byte chunk holding logical chunk c of tile row r (an XOR, so
+// it is its own inverse).  Depends on r only through r % 16.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (D == 128) {
@@ -65,14 +95,9 @@ __device__ __forceinline__ int swz(int r, int c) {
   }
 }
 
-template <int D>
-__device__ __forceinline__ int lds_off(int r, int c) {
-  return r * Geo<D>::ROW_BYTES + swz<D>(r, c) * 16;
-}
-
 // Number of entries <= x in the increasing array off[0, n); wave-cooperative
 // 64-way search (every lane returns the same value).
-__device__ int count_le(const int64_t* __restrict__ off, int64_t n, int64_t x) {
+__device__ int64_t count_le(const int64_t* __restrict__ off, int64_t n, int64_t x) {
   const int lane = threadIdx.x & 63;
   int64_t lo = 0, hi = n;
   while (hi - lo > 64) {
@@ -80,7 +105,7 @@ __device__ int count_le(const int64_t* __restrict__ off, int64_t n, int64_t x) {
     const int64_t idx = lo + lane * step;
     const bool p = idx < hi && off[idx] <= x;
     const int c = __popcll(__ballot(p));
-    if (c == 0) return (int)lo;
+    if (c == 0) return lo;
     const int64_t nlo = lo + (int64_t)(c - 1) * step + 1;
     const int64_t probe_c = lo + (int64_t)c * step;
     hi = probe_c < hi ? probe_c : hi;
@@ -88,7 +113,7 @@ __device__ int count_le(const int64_t* __restrict__ off, int64_t n, int64_t x) {
   }
   const int64_t idx = lo + lane;
   const bool p = idx < hi && off[idx] <= x;
-  return (int)(lo + __popcll(__ballot(p)));
+  return lo + __popcll(__ballot(p));
 }
 
 __device__ __forceinline__ float xhalf_max(float v) {
@@ -101,30 +126,23 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-__device__ __forceinline__ void load_tile(const __bf16* __restrict__ src, int64_t u0, int64_t Lk,
-                                          u32x4 (&reg)[Geo<D>::LOADS]) {
-  const int t = threadIdx.x;
-  const int c = t % Geo<D>::CHUNKS;
-#pragma unroll
-  for (int i = 0; i < Geo<D>::LOADS; ++i) {
-    const int r = t / Geo<D>::CHUNKS + i * Geo<D>::ROWS_PER_PASS;
-    int64_t u = u0 + r;
-    u = u < Lk ? u : Lk - 1;  // ragged tail: load a valid row, masked later
-    reg[i] = *reinterpret_cast<const u32x4*>(src + u * D + c * 8);
-  }
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+// Inline asm: the instruction has no register result, and hiding it from the
+// compiler keeps it from making unrelated LDS reads wait for it; completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the tile.
+__device__ __forceinline__ void copy16_saddr(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds)
+               : "memory");
 }
+__device__ __forceinline__ void copy16_vaddr(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int D>
-__device__ __forceinline__ void store_tile(lds_char* dst, const u32x4 (&reg)[Geo<D>::LOADS]) {
-  const int t = threadIdx.x;
-  const int c = t % Geo<D>::CHUNKS;
-#pragma unroll
-  for (int i = 0; i < Geo<D>::LOADS; ++i) {
-    const int r = t / Geo<D>::CHUNKS + i * Geo<D>::ROWS_PER_PASS;
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(dst + lds_off<D>(r, c)) = reg[i];
-  }
-}
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
@@ -133,12 +151,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     float* __restrict__ lse, int BH, int64_t Lq, int64_t Lk, int causal, float c_log2,
     int n_qtiles) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * G::TILE_BYTES];
-  lds_char* smem = (lds_char*)smem_raw;
+  constexpr int TB = G::TILE_BYTES;
+  constexpr int RB = G::ROW_BYTES;
+  constexpr int KK = G::KK;
+  constexpr int DB = G::DB;
+  __shared__ __attribute__((aligned(1024))) char k_lds_raw[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char v_lds_raw[2 * TB];
+  lds_char* const Kl = (lds_char*)k_lds_raw;
+  lds_char* const Vl = (lds_char*)v_lds_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
   const int l32 = lane & 31;
   const int bh = blockIdx.x % BH;
@@ -154,155 +178,282 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   float* Obh = O + (int64_t)bh * Lq * D;
   float* lse_bh = lse + (int64_t)bh * Lq;
 
-  int64_t n_lo = Lk, n_hi = Lk;
-  int64_t my_qpos = 0;
+  // Visible keys of a causal row are a prefix [0, n) of the block (positions
+  // increase).  n_lo / n_hi bound it for the whole tile; my_n is this row's.
+  int64_t n_lo = Lk, n_hi = Lk, my_n = Lk;
   if (causal) {
     n_lo = count_le(k_off, Lk, q_off[q_base]);
     n_hi = count_le(k_off, Lk, q_off[last_row]);
-    my_qpos = q_off[qrow_c];
+    const int64_t my_qpos = q_off[qrow_c];
+    int64_t lo = n_lo, hb = n_hi;  // first u in [n_lo, n_hi) with k_off[u] > my_qpos
+    while (lo < hb) {
+      const int64_t mid = (lo + hb) >> 1;
+      if (k_off[mid] <= my_qpos) lo = mid + 1; else hb = mid;
+    }
+    my_n = lo;
   }
 
   if (n_hi == 0) {  // no row of this tile sees any key of this block
-    if (qrow < Lq && hi == 0) lse_bh[qrow] = -INFINITY;
     if (qrow < Lq) {
-      float4 z = {0.f, 0.f, 0.f, 0.f};
+      if (hi == 0) lse_bh[qrow] = -INFINITY;
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
       for (int c = hi; c < D / 4; c += 2) reinterpret_cast<float4*>(Obh + qrow * D)[c] = z;
     }
     return;
   }
+  const int T = (int)((n_hi + BN - 1) / BN);
 
+  // ---- per-lane constants -------------------------------------------------
   // Q rows of this wave as the B operand: lane holds Q[qrow][kk*16 + hi*8 .. +7].
-  bf16x8 qf[D / 16];
+  bf16x8 qf[KK];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
+  for (int kk = 0; kk < KK; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(Qbh + qrow_c * D + kk * 16 + hi * 8);
+  // K operand of (kb, kk): tile row kb*32 + l32, logical chunk kk*2 + hi.
+  int koff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = l32 * RB + swz<D>(l32, kk * 2 + hi) * 16;
+  // V operand of (kb, half, db): two transposing reads of rows
+  // kb*32 + half*16 + vrow (+8), 8 bytes inside chunk db*4 + vch.
+  const int vrow = hi * 4 + ((lane & 15) >> 2);
+  const int vch = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+  const int vsub = (lane & 1) * 8;
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      voff[db][p] = (vrow + 8 * p) * RB + swz<D>(vrow + 8 * p, db * 4 + vch) * 16 + vsub;
+  // Copy instruction i of this wave fills tile rows (wv*IPW + i)*RPI + ...:
+  // lane takes physical chunk lane % CHUNKS of its row.
+  int coff[G::IPW];
+  int crow[G::IPW];
+#pragma unroll
+  for (int i = 0; i < G::IPW; ++i) {
+    const int n = wv * G::IPW + i;
+    crow[i] = n * G::RPI + lane / G::CHUNKS;
+    coff[i] = crow[i] * RB + swz<D>(crow[i], lane % G::CHUNKS) * 16;
+  }
 
-  f32x16 acc[D / 32];
+  auto copy_tile = [&](const __bf16* src, int j, lds_char* dst) __attribute__((always_inline)) {
+    const int64_t u0 = (int64_t)j * BN;
+    if (u0 + BN <= Lk) {
+      const __bf16* base = src + u0 * D;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+      for (int i = 0; i < G::IPW; ++i)
+        copy16_saddr((uint32_t)coff[i], base, lds_addr(dst + (wv * G::IPW + i) * 1024));
+    } else {  // last, ragged tile: rows past the block re-read the last row (masked later)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m2 = -INFINITY;  // running max of scaled scores, log2 units
-  float lsum = 0.f;      // this lane's share of the running sum
-
-  const int n_tiles = (int)((n_hi + BN - 1) / BN);
-  u32x4 kreg[G::LOADS], vreg[G::LOADS];
-  load_tile<D>(Kbh, 0, Lk, kreg);
-  load_tile<D>(Vbh, 0, Lk, vreg);
-  store_tile<D>(smem, kreg);
-  store_tile<D>(smem + G::TILE_BYTES, vreg);
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    lds_char* Ks = smem + buf * 2 * G::TILE_BYTES;
-    lds_char* Vs = Ks + G::TILE_BYTES;
-    const int64_t u0 = (int64_t)it * BN;
-    const bool more = it + 1 < n_tiles;
-    if (more) {
-      load_tile<D>(Kbh, u0 + BN, Lk, kreg);
-      load_tile<D>(Vbh, u0 + BN, Lk, vreg);
-    }
-
-    // S^T for keys u0 + kb*32 + [0, 32): lane holds keys kb*32 + (r/4)*8 + hi*4 + r%4.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
-            Ks + lds_off<D>(kb * 32 + l32, kk * 2 + hi));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+      for (int i = 0; i < G::IPW; ++i) {
+        int64_t u = u0 + crow[i];
+        u = u < Lk ? u : Lk - 1;
+        const char* g = (const char*)(src + u * D) + (coff[i] - crow[i] * RB);
+        copy16_vaddr(g, lds_addr(dst + (wv * G::IPW + i) * 1024));
       }
     }
+  };
 
-    if (u0 + BN > n_lo) {  // tile crosses a row's visibility bound or the end of the block
+  f32x16 acc[DB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  f32x16 s[2][NKB];        // scores of two tiles (S^T layout), by tile parity
+  bf16x8 pf[2][NKB][2];    // bf16 P of two tiles, by tile parity
+  float m2 = -INFINITY;  // exponent reference: an integer (log2 units) or -inf
+  float lsum = 0.f;      // this lane's share of the row sum of bf16 P (normalises O)
+  float lsum_f = 0.f;    // the same sum in fp32, before rounding (gives lse)
+  const f32x16 zero16 = {};
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Mask tile j's scores, find their row max and, when it outgrows the
+  // reference, raise the reference to the next integer and rescale O, l and
+  // the P of the tile computed last (`pprev`, not yet multiplied into O).
+  auto finish_scores = [&](int j, f32x16 (&sj)[NKB], bf16x8 (&pprev)[NKB][2], auto HAS_PREV_)
+                           __attribute__((always_inline)) {
+    constexpr bool HAS_PREV = decltype(HAS_PREV_)::value;
+    const int64_t u0 = (int64_t)j * BN;
+    if (u0 + BN > n_lo) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t u = u0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          const bool vis = u < Lk && (!causal || k_off[u] <= my_qpos);
-          if (!vis) s[kb][r] = -INFINITY;
+          if (u >= my_n) sj[kb][r] = -INFINITY;
         }
     }
-
-    float mx = s[0][0];
+    float mx = sj[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m2, mx * c_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
-    if (__ballot(m_new > m2)) {
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sj[kb][r]);
+    const float mx2 = xhalf_max(mx) * c_log2;
+    if (__ballot(mx2 > m2 + RESCALE_LOG2)) {
+      const float m_new = ceilf(fmaxf(m2, mx2));
+      const int k = (m2 == -INFINITY || m_new == -INFINITY) ? 0 : (int)(m2 - m_new);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      lsum *= alpha;
+        for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_amdgcn_ldexpf(acc[db][r], k);
+      lsum = __builtin_amdgcn_ldexpf(lsum, k);
+      lsum_f = __builtin_amdgcn_ldexpf(lsum_f, k);
+      if constexpr (HAS_PREV) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              pprev[kb][h][e] = (__bf16)__builtin_amdgcn_ldexpf((float)pprev[kb][h][e], k);
+      }
+      m2 = m_new;
     }
-    m2 = m_new;
+  };
 
-    bf16x8 pf[2][2];
-    float ps = 0.f;
+  // One pipeline iteration for tile t (parity P): copies of K(t+2), V(t);
+  // PV(t-1) and QK^T(t+1) on the matrix cores interleaved with the exp2 of
+  // tile t; then the row max of tile t+1.
+  auto iter = [&](int t, auto P_, auto PV_, auto QK_) __attribute__((always_inline)) {
+    constexpr int P = decltype(P_)::value;
+    constexpr bool HAS_PV = decltype(PV_)::value;
+    constexpr bool HAS_QK = decltype(QK_)::value;
+    if (t + 2 < T) copy_tile(Kbh, t + 2, Kl + P * TB);
+    copy_tile(Vbh, t, Vl + P * TB);
+
+    const float m_use = m2 == -INFINITY ? 0.f : m2;
+    const lds_char* Kt = Kl + (P ^ 1) * TB;  // K(t+1)
+    const lds_char* Vt = Vl + (P ^ 1) * TB;  // V(t-1)
+    constexpr int NV = HAS_PV ? 2 * NKB * DB : 0;
+    constexpr int NQ = HAS_QK ? NKB * KK : 0;
+    constexpr int NM = NV + NQ;
+    constexpr int PF = 3;  // operands in flight ahead of the MFMA using them
+    auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      if (i < NV) {
+        const int kb = i / (2 * DB), half = (i / DB) & 1, db = i % DB;
+        const lds_char* b = Vt + (kb * 32 + half * 16) * RB;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(b + voff[db][0]));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(b + voff[db][1]));
+        const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        return __builtin_bit_cast(bf16x8, v8);
+      }
+      const int q = i - NV, kb = q / KK, kk = q % KK;
+      return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+          Kt + kb * 32 * RB + koff[kk]);
+    };
+    bf16x8 ob[PF];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < PF && i < NM; ++i) ob[i] = fetch(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const bf16x8 cur = ob[i % PF];
+      if (i + PF < NM) ob[i % PF] = fetch(i + PF);
+      if (i < NV) {
+        const int kb = i / (2 * DB), half = (i / DB) & 1, db = i % DB;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][kb][half], acc[db], 0,
+                                                          0, 0);
+      } else {
+        const int q = i - NV, kb = q / KK, kk = q % KK;
+        s[P ^ 1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            cur, qf[kk], kk == 0 ? zero16 : s[P ^ 1][kb], 0, 0, 0);
+      }
+    }
+    // exp2 of tile t, packed to bf16; row sums of the fp32 and of the packed values.
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -m_use));
-        ps += p;
-        pf[kb][r >> 3][r & 7] = (__bf16)p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[P][kb][r], c_log2, -m_use));
+        lsum_f += p;
+        pf[P][kb][r >> 3][r & 7] = (__bf16)p;
       }
-    lsum += ps;
-
-    // O^T += V^T P^T.  A operand: lane holds V[key slot][d = db*32 + l32] for the
-    // eight key slots matching pf's registers, fetched as two transposing reads.
-    const int g = lane >> 4;
-    const int vrow = hi * 4 + ((lane & 15) >> 2);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int r0 = kb * 32 + half * 16 + vrow;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int ch = db * 4 + (g & 1) * 2 + ((lane >> 1) & 1);
-          const int sub = (lane & 1) * 8;
-          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(Vs + lds_off<D>(r0, ch) + sub));
-          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(Vs + lds_off<D>(r0 + 8, ch) + sub));
-          const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
-                                                            pf[kb][half], acc[db], 0, 0, 0);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pair = {pf[P][kb][h][e], pf[P][kb][h][e + 1]};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
         }
-      }
-
-    if (more) {
-      lds_char* nK = smem + (buf ^ 1) * 2 * G::TILE_BYTES;
-      store_tile<D>(nK, kreg);
-      store_tile<D>(nK + G::TILE_BYTES, vreg);
-    }
+    if constexpr (HAS_QK) finish_scores(t + 1, s[P ^ 1], pf[P], std::true_type{});
+    wait_copies();
     __syncthreads();
+  };
+
+  // Prologue: K(0), K(1) into LDS; scores of tile 0.
+  copy_tile(Kbh, 0, Kl);
+  if (T > 1) copy_tile(Kbh, 1, Kl + TB);
+  wait_copies();
+  __syncthreads();
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(Kl + kb * 32 * RB +
+                                                                             koff[kk]),
+          qf[kk], kk == 0 ? zero16 : s[0][kb], 0, 0, 0);
+  finish_scores(0, s[0], pf[0], std::false_type{});
+  __syncthreads();  // K(0) is read; its buffer is refilled by iteration 0
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::true_type;
+  using BF = std::false_type;
+  if (T == 1) {
+    iter(0, I0{}, BF{}, BF{});
+  } else {
+    iter(0, I0{}, BF{}, BT{});
+    int t = 1;
+    for (; t + 2 < T; t += 2) {
+      iter(t, I1{}, BT{}, BT{});
+      iter(t + 1, I0{}, BT{}, BT{});
+    }
+    if (t == T - 2) {
+      if (t & 1) iter(t, I1{}, BT{}, BT{}); else iter(t, I0{}, BT{}, BT{});
+      ++t;
+    }
+    if (t & 1) iter(t, I1{}, BT{}, BF{}); else iter(t, I0{}, BT{}, BF{});
   }
 
+  // Epilogue: PV(T-1).
+  auto last_pv = [&](auto P_) __attribute__((always_inline)) {
+    constexpr int P = decltype(P_)::value;
+    const lds_char* Vt = Vl + P * TB;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const lds_char* b = Vt + (kb * 32 + half * 16) * RB;
+          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(b + voff[db][0]));
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(b + voff[db][1]));
+          const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
+                                                            pf[P][kb][half], acc[db], 0, 0, 0);
+        }
+  };
+  if ((T - 1) & 1) last_pv(I1{}); else last_pv(I0{});
+
   const float ltot = xhalf_sum(lsum);
+  const float ltot_f = xhalf_sum(lsum_f);
   if (qrow < Lq) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     float* orow = Obh + qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        float4 v = {acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv,
-                    acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
+        const float4 v = {acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv,
+                          acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
         *reinterpret_cast<float4*>(orow + db * 32 + gq * 8 + hi * 4) = v;
       }
-    if (hi == 0) lse_bh[qrow] = ltot > 0.f ? (m2 + __log2f(ltot)) * LN2 : -INFINITY;
+    if (hi == 0) lse_bh[qrow] = ltot_f > 0.f ? (m2 + __log2f(ltot_f)) * LN2 : -INFINITY;
   }
 }
 
