@@ -2,16 +2,19 @@
 
 A step is one pass of the whole hot path for the rank: zigzag-permute the
 global K and V (all ranks' shares, which the ring visits) and the rank's Q,
-run the rank's ring (N partial-attention launches in ring order, N-1
-online-softmax merges), and scatter O and lse back to global token order.
-Inputs are resident in HBM before timing starts.
+run the rank's ring, and scatter O and lse back to global token order.  The
+ring is one launch that walks the N K/V blocks in ring order and folds each
+block into the running result by online softmax in registers
+(cpa_rank_forward_fused); `--ring partials` runs it as N partial-attention
+launches and N-1 merge launches instead (cpa_rank_forward).  Inputs are
+resident in HBM before timing starts.
 
 Metric: causal-useful attention TFLOP/s = 4 * D * B * H * P / t, where P is the
 number of (query, key) pairs the rank's queries may see (key position <= query
 position), i.e. masked and skipped work is not counted.
 
-Prints ONE JSON line.  `roofline` is for the dominant kernel (partial
-attention, bf16 MFMA-bound): its useful FLOP per launch over its average launch
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the attention
+kernel, bf16 MFMA-bound): its useful FLOP per launch over its average launch
 duration, timed with HIP events on the launch stream.  `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same share's query rows.
 """
@@ -27,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
 PEAK_HBM_GBS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "partial_attn_128k_pmc.json")
+PMC_FILES = {"fused": os.path.join(ROOT, "profiles", "ring_fused_128k_pmc.json"),
+             "partials": os.path.join(ROOT, "profiles", "partial_attn_128k_pmc.json")}
 KERNEL_SRC = os.path.join(ROOT, "sequence_attention_cpa_amd", "csrc", "partial_attn.hip")
 
 
@@ -41,11 +45,11 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic():
-    """HBM bytes per partial launch from committed rocprofv3 counter runs, or
-    None when they were taken on a different version of the kernel."""
+def pmc_traffic(ring):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter runs, or None when they were taken on a different version of it."""
     try:
-        with open(PMC_FILE) as f:
+        with open(PMC_FILES[ring]) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -113,6 +117,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="128k")
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--ring", choices=("fused", "partials"), default="fused",
+                    help="one fused launch per ring (default) or N partials + N-1 merges")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -137,7 +143,9 @@ def main():
     rank = args.rank
     Qh, Kh, Vh, _ = make_inputs(w)
     Q, K, V = Qh.to(dev), Kh.to(dev), Vh.to(dev)
-    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, dev, rank, rank + 1)
+    fused = args.ring == "fused"
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, dev, rank, rank + 1,
+                         fused=fused)
     pos = pipe.pos_host.numpy()
     if w.causal:
         pairs = [causal_pairs(pos[rank], pos[j]) for j in range(w.N)]
@@ -169,40 +177,52 @@ def main():
     ms_step = wall / args.steps * 1e3
     ms_step_ev = ev0.elapsed_time(ev1) / args.steps
 
-    # Per-kernel timing on the same stream: the ring's partials (same kernel,
-    # same arguments as inside the rank's ring), its merges, and the permutes.
+    # Per-kernel timing on the same stream: the fused ring launch, the ring's
+    # partials (same kernel and arguments as inside cpa_rank_forward), its
+    # merges, and the K permute.
     Lr = w.Lr
     tO = torch.empty((w.B, w.H, Lr, w.D), dtype=torch.float32, device=dev)
     tl = torch.empty((w.B, w.H, Lr), dtype=torch.float32, device=dev)
     pos_d = pipe.pos
     reps = max(1, args.steps // 2)
-    evs = []
+
+    def timed(fn, n):
+        evs = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        return evs
+
+    fused_evs = []
+    if w.dtype == "bf16" and w.D in (64, 128):
+        fused_evs = timed(lambda: cpa.rank_forward_fused(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr,
+                                                         pos_d, w.causal, out=tO, lse=tl), reps)
+    part_evs = []
     for _ in range(reps):
         for s in range(w.N):
             j = (rank + s) % w.N
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            cpa.partial(pipe.Qr[0], pipe.Kr[j], pipe.Vr[j], pos_d[rank], pos_d[j], w.causal,
-                        out=tO, lse=tl)
-            b.record(stream)
-            evs.append((j, a, b))
-    mevs, pevs = [], []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        cpa.merge(pipe.Or[0], pipe.lser[0], tO, tl)
-        b.record(stream)
-        mevs.append((a, b))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr)
-        b.record(stream)
-        pevs.append((a, b))
+            part_evs += [(j, e) for e in timed(lambda: cpa.partial(
+                pipe.Qr[0], pipe.Kr[j], pipe.Vr[j], pos_d[rank], pos_d[j], w.causal, out=tO,
+                lse=tl), 1)]
+    mevs = timed(lambda: cpa.merge(pipe.Or[0], pipe.lser[0], tO, tl), reps)
+    pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr), reps)
     torch.cuda.synchronize()
-    p_ms = np.array([a.elapsed_time(b) for _, a, b in evs])
-    p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _, _ in evs])
+    p_ms = np.array([a.elapsed_time(b) for _, (a, b) in part_evs])
+    p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _ in part_evs])
     p_avg_ms = float(p_ms.mean())
-    achieved = float(p_flops.mean() / (p_avg_ms * 1e-3) / 1e12)
+    f_ms = np.array([a.elapsed_time(b) for a, b in fused_evs]) if fused_evs else None
+    if fused:
+        dom_kernel = f"partial_attn_mfma_kernel<{w.D}> (one launch, {w.N} K/V blocks)"
+        dom_ms = float(f_ms.mean())
+        dom_flop = useful
+    else:
+        dom_kernel = f"partial_attn_mfma_kernel<{w.D}> (one K/V block)"
+        dom_ms = p_avg_ms
+        dom_flop = float(p_flops.mean())
+    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
     m_ms = float(np.mean([a.elapsed_time(b) for a, b in mevs]))
     m_bytes = w.B * w.H * Lr * (w.D + 1) * 4 * 3  # read acc + new, write acc (O and lse)
     perm_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
@@ -230,11 +250,13 @@ def main():
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": pmc_traffic(), "kernel": "partial_attn_mfma_kernel<128>",
-                     "avg_launch_ms": round(p_avg_ms, 4),
-                     "useful_flop_per_launch": float(p_flops.mean())},
+                     "traffic": pmc_traffic(args.ring), "kernel": dom_kernel,
+                     "avg_launch_ms": round(dom_ms, 4), "useful_flop_per_launch": dom_flop},
         "kernels": {
+            "ring": args.ring,
+            "fused_ring_ms": round(float(f_ms.mean()), 4) if f_ms is not None else None,
             "partial_ms": [round(float(x), 4) for x in p_ms[: w.N]],
+            "partial_TFLOP/s": round(float(p_flops.mean()) / (p_avg_ms * 1e-3) / 1e12, 2),
             "merge": {"ms": round(m_ms, 4), "GB/s": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
                       "bytes": m_bytes},
             "permute_K": {"ms": round(perm_ms, 4),

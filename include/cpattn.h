@@ -128,6 +128,21 @@ cpa_status cpa_rank_forward(int32_t i, int32_t N, const void *Q_i, const void *K
                             size_t ws_bytes, void *stream);
 
 /*
+ * Rank i's whole ring in ONE launch: the same result as cpa_rank_forward, but
+ * the kernel walks the N K/V blocks itself in ring order j = i, i+1, ...
+ * (mod N) and keeps the online-softmax state (O, running max, sums) in
+ * registers from one block to the next ("序列与上下文并行", 上下文并行: the
+ * partial results are folded incrementally), so no partial O is written and
+ * no merge pass runs.  Arguments as for cpa_rank_forward, without workspace.
+ * bf16 with D = 64 or 128 only (CPA_EUNSUPPORTED otherwise; use
+ * cpa_rank_forward for fp32 or D = 16).
+ */
+cpa_status cpa_rank_forward_fused(int32_t i, int32_t N, const void *Q_i, const void *K_all,
+                                  const void *V_all, const int64_t *pos_all, cpa_dtype dt,
+                                  int32_t B, int32_t H, int64_t L, int32_t D, int32_t causal,
+                                  float scale, float *O_i, float *lse_i, void *stream);
+
+/*
  * Permutation between global order and rank-major zigzag order, for ranks
  * [rank_lo, rank_hi) (the data-pipeline step of "序列与上下文并行", 工程实践:
  * each rank's data must follow the CP layout).

@@ -12,7 +12,7 @@ from ._lib import (CPA_BF16, CPA_F32, CpaError, check, last_error, load,  # noqa
                    version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
-           "zigzag_permute", "last_error", "version", "CpaError"]
+           "rank_forward_fused", "zigzag_permute", "last_error", "version", "CpaError"]
 
 
 def _torch():
@@ -107,6 +107,22 @@ def rank_forward(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool, scale
                                   _dtype_code(Q_i), B, H, L, D, int(bool(causal)), float(scale),
                                   _ptr(out), _ptr(lse), _ptr(workspace),
                                   0 if workspace is None else workspace.numel(), _stream(Q_i)))
+    return out, lse
+
+
+def rank_forward_fused(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
+                       scale: float = 0.0, out=None, lse=None):
+    """Rank i's ring in one launch (bf16, D = 64 or 128); same result as rank_forward."""
+    torch = _torch()
+    B, H, Lr, D = Q_i.shape
+    if out is None:
+        out = torch.empty((B, H, Lr, D), dtype=torch.float32, device=Q_i.device)
+    if lse is None:
+        lse = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
+    _need_gpu(Q_i, K_all, V_all, pos_all, out, lse)
+    check(load().cpa_rank_forward_fused(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
+                                        _dtype_code(Q_i), B, H, Lr * N, D, int(bool(causal)),
+                                        float(scale), _ptr(out), _ptr(lse), _stream(Q_i)))
     return out, lse
 
 

@@ -14,6 +14,14 @@ hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V,
                                float* lse, int BH, int64_t Lq, int64_t Lk, int D, bool causal,
                                float scale, hipStream_t stream);
 
+// Rank i's whole ring in one launch: Q_i [BH, Lr, D] against the N blocks of
+// rank-major K_all / V_all [N, BH, Lr, D] (positions pos_all [N, Lr]) in ring
+// order i, i+1, ..., online-softmax state kept in registers (D = 64 or 128).
+hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_all,
+                            const int64_t* q_off, const int64_t* pos_all, float* O, float* lse,
+                            int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
+                            hipStream_t stream);
+
 // Partial attention, one query row per thread, fp32 arithmetic throughout
 // (fp32 inputs, and bf16 inputs with D = 16).
 hipError_t launch_partial_rowwise(const void* Q, const void* K, const void* V, bool bf16,

@@ -194,6 +194,26 @@ cpa_status cpa_rank_forward(int32_t i, int32_t N, const void* Q_i, const void* K
   return ok();
 }
 
+cpa_status cpa_rank_forward_fused(int32_t i, int32_t N, const void* Q_i, const void* K_all,
+                                  const void* V_all, const int64_t* pos_all, cpa_dtype dt,
+                                  int32_t B, int32_t H, int64_t L, int32_t D, int32_t causal,
+                                  float scale, float* O_i, float* lse_i, void* stream) {
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (i < 0 || i >= N) return fail(CPA_EINVAL, "rank index %d outside [0, %d)", i, N);
+  if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
+  const int64_t Lr = L / N;
+  st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, O_i, lse_i);
+  if (st != CPA_OK) return st;
+  if (dt != CPA_BF16 || (D != 64 && D != 128))
+    return fail(CPA_EUNSUPPORTED, "fused ring needs bf16 with D = 64 or 128 (use cpa_rank_forward)");
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
+  return from_hip(cpa::launch_ring_mfma(Q_i, K_all, V_all, pos_all + (int64_t)i * Lr, pos_all, O_i,
+                                        lse_i, B * H, Lr, N, i, D, causal != 0, scale,
+                                        (hipStream_t)stream),
+                  "fused ring launch");
+}
+
 cpa_status cpa_zigzag_permute(const void* src, void* dst, int32_t elem_bytes, int32_t B,
                               int32_t H, int64_t L, int32_t D, const int64_t* pos_all, int32_t N,
                               int32_t rank_lo, int32_t rank_hi, int32_t inverse, void* stream) {

@@ -144,12 +144,17 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
 
+// Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
+// K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
+// the order b = first, first + 1, ... (mod nblk).  One block is one ring step
+// (cpa_partial); nblk = N with first = i is rank i's whole ring, the running
+// (O, max, sums) staying in registers from one block to the next.
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ O,
-    float* __restrict__ lse, int BH, int64_t Lq, int64_t Lk, int causal, float c_log2,
-    int n_qtiles) {
+    float* __restrict__ lse, int BH, int64_t Lq, int64_t Lk, int64_t kv_stride,
+    int64_t koff_stride, int nblk, int first, int causal, float c_log2, int n_qtiles) {
   using G = Geo<D>;
   constexpr int TB = G::TILE_BYTES;
   constexpr int RB = G::ROW_BYTES;
@@ -173,35 +178,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   const int64_t qrow_c = qrow < Lq ? qrow : Lq - 1;
 
   const __bf16* Qbh = Q + (int64_t)bh * Lq * D;
-  const __bf16* Kbh = K + (int64_t)bh * Lk * D;
-  const __bf16* Vbh = V + (int64_t)bh * Lk * D;
   float* Obh = O + (int64_t)bh * Lq * D;
   float* lse_bh = lse + (int64_t)bh * Lq;
+  const int64_t q_first = causal ? q_off[q_base] : 0;
+  const int64_t q_last = causal ? q_off[last_row] : 0;
+  const int64_t my_qpos = causal ? q_off[qrow_c] : 0;
 
-  // Visible keys of a causal row are a prefix [0, n) of the block (positions
-  // increase).  n_lo / n_hi bound it for the whole tile; my_n is this row's.
+  // Current block: pointers, and the visible-key bounds.  Visible keys of a
+  // causal row are a prefix [0, n) of the block (positions increase); n_lo /
+  // n_hi bound it for the whole tile, my_n is this row's.
+  const __bf16* Kbh = nullptr;
+  const __bf16* Vbh = nullptr;
   int64_t n_lo = Lk, n_hi = Lk, my_n = Lk;
-  if (causal) {
-    n_lo = count_le(k_off, Lk, q_off[q_base]);
-    n_hi = count_le(k_off, Lk, q_off[last_row]);
-    const int64_t my_qpos = q_off[qrow_c];
-    int64_t lo = n_lo, hb = n_hi;  // first u in [n_lo, n_hi) with k_off[u] > my_qpos
-    while (lo < hb) {
-      const int64_t mid = (lo + hb) >> 1;
-      if (k_off[mid] <= my_qpos) lo = mid + 1; else hb = mid;
-    }
-    my_n = lo;
-  }
-
-  if (n_hi == 0) {  // no row of this tile sees any key of this block
-    if (qrow < Lq) {
-      if (hi == 0) lse_bh[qrow] = -INFINITY;
-      const float4 z = {0.f, 0.f, 0.f, 0.f};
-      for (int c = hi; c < D / 4; c += 2) reinterpret_cast<float4*>(Obh + qrow * D)[c] = z;
-    }
-    return;
-  }
-  const int T = (int)((n_hi + BN - 1) / BN);
+  int T = 0;
 
   // ---- per-lane constants -------------------------------------------------
   // Q rows of this wave as the B operand: lane holds Q[qrow][kk*16 + hi*8 .. +7].
@@ -382,6 +371,29 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     __syncthreads();
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::true_type;
+  using BF = std::false_type;
+
+  for (int sb = 0; sb < nblk; ++sb) {
+  const int blk = (first + sb) % nblk;
+  Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
+  Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
+  if (causal) {
+    const int64_t* kb_off = k_off + blk * koff_stride;
+    n_lo = count_le(kb_off, Lk, q_first);
+    n_hi = count_le(kb_off, Lk, q_last);
+    int64_t lo = n_lo, hb = n_hi;  // first u in [n_lo, n_hi) with position > my_qpos
+    while (lo < hb) {
+      const int64_t mid = (lo + hb) >> 1;
+      if (kb_off[mid] <= my_qpos) lo = mid + 1; else hb = mid;
+    }
+    my_n = lo;
+  }
+  if (n_hi == 0) continue;  // no row of this tile sees any key of this block
+  T = (int)((n_hi + BN - 1) / BN);
+
   // Prologue: K(0), K(1) into LDS; scores of tile 0.
   copy_tile(Kbh, 0, Kl);
   if (T > 1) copy_tile(Kbh, 1, Kl + TB);
@@ -398,10 +410,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   finish_scores(0, s[0], pf[0], std::false_type{});
   __syncthreads();  // K(0) is read; its buffer is refilled by iteration 0
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using BT = std::true_type;
-  using BF = std::false_type;
   if (T == 1) {
     iter(0, I0{}, BF{}, BF{});
   } else {
@@ -439,6 +447,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
         }
   };
   if ((T - 1) & 1) last_pv(I1{}); else last_pv(I0{});
+  __syncthreads();  // the next block refills both LDS buffers
+  }  // blocks
 
   const float ltot = xhalf_sum(lsum);
   const float ltot_f = xhalf_sum(lsum_f);
@@ -459,22 +469,42 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
 
 }  // namespace
 
-hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V, const int64_t* q_off,
-                               const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
-                               int64_t Lk, int D, bool causal, float scale, hipStream_t stream) {
+namespace {
+hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int64_t* q_off,
+                         const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
+                         int64_t Lk, int64_t kv_stride, int64_t koff_stride, int nblk, int first,
+                         int D, bool causal, float scale, hipStream_t stream) {
   const int n_qtiles = (int)((Lq + BM - 1) / BM);
   const dim3 grid((unsigned)(n_qtiles * BH));
   const float c_log2 = scale * LOG2E;
   if (D == 128) {
     hipLaunchKernelGGL(partial_attn_mfma_kernel<128>, grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
-                       BH, Lq, Lk, causal ? 1 : 0, c_log2, n_qtiles);
+                       BH, Lq, Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0, c_log2,
+                       n_qtiles);
   } else {
     hipLaunchKernelGGL(partial_attn_mfma_kernel<64>, grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
-                       BH, Lq, Lk, causal ? 1 : 0, c_log2, n_qtiles);
+                       BH, Lq, Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0, c_log2,
+                       n_qtiles);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V, const int64_t* q_off,
+                               const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
+                               int64_t Lk, int D, bool causal, float scale, hipStream_t stream) {
+  return launch_blocks(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, 0, 0, 1, 0, D, causal, scale,
+                       stream);
+}
+
+hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_all,
+                            const int64_t* q_off, const int64_t* pos_all, float* O, float* lse,
+                            int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
+                            hipStream_t stream) {
+  return launch_blocks(Q_i, K_all, V_all, q_off, pos_all, O, lse, BH, Lr, Lr, (int64_t)BH * Lr * D,
+                       Lr, N, i, D, causal, scale, stream);
 }
 
 }  // namespace cpa

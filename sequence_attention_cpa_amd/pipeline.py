@@ -7,20 +7,26 @@ merges), and scatter the ranks' O and lse back to global token order.  On one
 GPU the other ranks' K/V shares are slices of the same buffers, so the ring
 needs no communication.
 
+With `fused=True` each rank's ring is one launch (cpa_rank_forward_fused:
+the online-softmax state stays in registers across the N blocks) instead of
+N partial launches and N-1 merges; bf16 with D = 64 or 128 only.
+
 All buffers are allocated once in the constructor; `step` allocates nothing.
 """
 from __future__ import annotations
 
-from . import rank_forward, rank_forward_workspace, zigzag_layout, zigzag_permute
+from . import (rank_forward, rank_forward_fused, rank_forward_workspace, zigzag_layout,
+               zigzag_permute)
 
 
 class SharePipeline:
     def __init__(self, B: int, H: int, L: int, D: int, N: int, causal: bool, dtype, device,
-                 rank_lo: int = 0, rank_hi: int | None = None, scale: float = 0.0):
+                 rank_lo: int = 0, rank_hi: int | None = None, scale: float = 0.0,
+                 fused: bool = False):
         import torch
 
         self.B, self.H, self.L, self.D, self.N = B, H, L, D, N
-        self.causal, self.scale = causal, scale
+        self.causal, self.scale, self.fused = causal, scale, fused
         self.rank_lo = rank_lo
         self.rank_hi = N if rank_hi is None else rank_hi
         nr = self.rank_hi - self.rank_lo
@@ -32,8 +38,8 @@ class SharePipeline:
         self.Qr = torch.empty((nr, B, H, Lr, D), dtype=dtype, device=device)
         self.Or = torch.empty((nr, B, H, Lr, D), dtype=torch.float32, device=device)
         self.lser = torch.empty((nr, B, H, Lr), dtype=torch.float32, device=device)
-        self.ws = torch.empty(max(rank_forward_workspace(B, H, L, N, D), 1), dtype=torch.uint8,
-                              device=device)
+        ws_bytes = 1 if fused else max(rank_forward_workspace(B, H, L, N, D), 1)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.O = torch.zeros((B, H, L, D), dtype=torch.float32, device=device)
         self.lse = torch.full((B, H, L), float("-inf"), dtype=torch.float32, device=device)
 
@@ -52,5 +58,9 @@ class SharePipeline:
     def ring(self):
         """The ring part only (inputs already rank-major)."""
         for k, i in enumerate(range(self.rank_lo, self.rank_hi)):
-            rank_forward(i, self.N, self.Qr[k], self.Kr, self.Vr, self.pos, self.causal,
-                         self.scale, out=self.Or[k], lse=self.lser[k], workspace=self.ws)
+            if self.fused:
+                rank_forward_fused(i, self.N, self.Qr[k], self.Kr, self.Vr, self.pos, self.causal,
+                                   self.scale, out=self.Or[k], lse=self.lser[k])
+            else:
+                rank_forward(i, self.N, self.Qr[k], self.Kr, self.Vr, self.pos, self.causal,
+                             self.scale, out=self.Or[k], lse=self.lser[k], workspace=self.ws)

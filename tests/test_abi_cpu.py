@@ -166,6 +166,31 @@ def test_rank_forward_rejects(lib, kw, status):
     assert cpa.last_error() != ""
 
 
+def _fused(lib, **kw):
+    a = dict(i=0, N=4, Q=P, K=P, V=P, pos=P, dt=_lib.CPA_BF16, B=1, H=2, L=256, D=128, causal=1,
+             scale=0.0, O=P, lse=P, stream=None)
+    a.update(kw)
+    return lib.cpa_rank_forward_fused(a["i"], a["N"], a["Q"], a["K"], a["V"], a["pos"], a["dt"],
+                                      a["B"], a["H"], a["L"], a["D"], a["causal"], a["scale"],
+                                      a["O"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(i=4), _lib.CPA_EINVAL),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(L=260), _lib.CPA_ESHAPE),
+    (dict(dt=_lib.CPA_F32), _lib.CPA_EUNSUPPORTED),
+    (dict(D=16), _lib.CPA_EUNSUPPORTED),
+    (dict(D=48), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=5), _lib.CPA_EDTYPE),
+    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(O=P + 4), _lib.CPA_EINVAL),
+])
+def test_rank_forward_fused_rejects(lib, kw, status):
+    assert _fused(lib, **kw) == status
+    assert cpa.last_error() != ""
+
+
 def _perm(lib, **kw):
     a = dict(src=P, dst=P, eb=2, B=1, H=2, L=256, D=128, pos=P, N=4, lo=0, hi=4, inv=0, stream=None)
     a.update(kw)

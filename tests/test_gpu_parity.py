@@ -257,8 +257,8 @@ def test_permute_bit_exact(dtype, D, ranks):
 
 # ------------------------------------------------------------ rank forward
 
-def stitched_all_ranks(w, Q, K, V):
-    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV)
+def stitched_all_ranks(w, Q, K, V, fused=False):
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=fused)
     O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     torch.cuda.synchronize()
     return O.cpu().double().numpy(), lse.cpu().double().numpy()
@@ -275,9 +275,10 @@ def test_rank_forward_tiny_f32_all_ranks():
 def test_rank_forward_demo_bf16_all_ranks():
     w = WORKLOADS["demo"]
     Q, K, V, _ = make_inputs(w)
-    O, lse = stitched_all_ranks(w, Q, K, V)
     Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), w.causal)
-    assert_bf16_close(O, lse, Or, lr, "demo")
+    for fused in (False, True):
+        O, lse = stitched_all_ranks(w, Q, K, V, fused)
+        assert_bf16_close(O, lse, Or, lr, f"demo fused={fused}")
 
 
 def test_rank_forward_12k_all_ranks_every_row():
@@ -285,38 +286,49 @@ def test_rank_forward_12k_all_ranks_every_row():
     say("12k: generating")
     Q, K, V, _ = make_inputs(w)
     say("12k: GPU")
-    O, lse = stitched_all_ranks(w, Q, K, V)
+    outs = {f: stitched_all_ranks(w, Q, K, V, f) for f in (False, True)}
     say("12k: oracle")
     rows = {(b, h): np.arange(w.L) for b in range(w.B) for h in range(w.H)}
     ref = oracle_rows(lambda b, h: widen(Q[b, h]), lambda b, h: widen(K[b, h]),
                       lambda b, h: widen(V[b, h]), rows, w.causal)
     Or = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
     lr = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
-    mx, mean = assert_bf16_close(O, lse, Or, lr, "12k")
-    say(f"12k: max {mx:.3e} mean {mean:.3e}")
+    for f, (O, lse) in outs.items():
+        mx, mean = assert_bf16_close(O, lse, Or, lr, f"12k fused={f}")
+        say(f"12k fused={f}: max {mx:.3e} mean {mean:.3e}")
 
 
 def share_check(name, rank, n_rows, block):
     w = WORKLOADS[name]
     say(f"{name}: generating")
     Q, K, V, outl = make_inputs(w)
-    say(f"{name}: GPU rank {rank}")
-    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, rank, rank + 1)
-    Od, lsed = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
-    pos = pipe.pos_host.numpy()
-    t = sample_rows(w, rank, pos[rank], n_rows // (w.B * w.H), outl)
-    g = pos[rank][t]
-    O = Od[:, :, torch.from_numpy(g).to(DEV)].cpu().double().numpy()
-    lse = lsed[:, :, torch.from_numpy(g).to(DEV)].cpu().double().numpy()
-    torch.cuda.synchronize()
+    Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
+    results = {}
+    pos = None
+    for fused in (False, True):
+        say(f"{name}: GPU rank {rank} fused={fused}")
+        pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, rank, rank + 1,
+                             fused=fused)
+        Od, lsed = pipe.step(Qd, Kd, Vd)
+        pos = pipe.pos_host.numpy()
+        if "g" not in results:
+            t = sample_rows(w, rank, pos[rank], n_rows // (w.B * w.H), outl)
+            results["g"] = pos[rank][t]
+        gi = torch.from_numpy(results["g"]).to(DEV)
+        results[fused] = (Od[:, :, gi].cpu().double().numpy(), lsed[:, :, gi].cpu().double().numpy())
+        del pipe, Od, lsed
+        torch.cuda.synchronize()
+    g = results["g"]
     say(f"{name}: oracle on {len(g)} rows x {w.B * w.H} heads")
     rows = {(b, h): g for b in range(w.B) for h in range(w.H)}
     ref = oracle_rows(lambda b, h: widen(Q[b, h]), lambda b, h: widen(K[b, h]),
                       lambda b, h: widen(V[b, h]), rows, w.causal, block=block)
     Or = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
     lr = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
-    mx, mean = assert_bf16_close(O, lse, Or, lr, name)
-    say(f"{name}: max {mx:.3e} mean {mean:.3e}")
+    for fused in (False, True):
+        O, lse = results[fused]
+        mx, mean = assert_bf16_close(O, lse, Or, lr, f"{name} fused={fused}")
+        say(f"{name} fused={fused}: max {mx:.3e} mean {mean:.3e}")
 
 
 @pytest.mark.parametrize("rank", [0, 3])
@@ -327,3 +339,29 @@ def test_rank_forward_128k_share_sampled(rank):
 @pytest.mark.timeout(900)
 def test_rank_forward_1m_share_sampled():
     share_check("1m", 0, 256, 8)
+
+
+FUSED_CASES = [
+    # B, H, L, N, D, causal
+    (2, 2, 2048, 1, 128, True),
+    (1, 2, 2048, 2, 128, True),
+    (1, 3, 4096, 8, 128, True),
+    (2, 2, 1024, 4, 64, True),
+    (1, 2, 1536, 4, 128, False),
+    (1, 2, 256, 16, 128, True),   # chunks of 8 keys: every tile of every block is masked
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[str(c) for c in FUSED_CASES])
+def test_rank_forward_fused_small_shapes(case):
+    """The one-launch ring equals the oracle for every rank, at shapes that span
+    several tiles, ragged tails, N = 1 and chunks shorter than a tile."""
+    B, H, L, N, D, causal = case
+    Q = rand((B, H, L, D), torch.bfloat16, 60)
+    K = rand((B, H, L, D), torch.bfloat16, 61)
+    V = rand((B, H, L, D), torch.bfloat16, 62)
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), causal)
+    pipe = SharePipeline(B, H, L, D, N, causal, Q.dtype, DEV, fused=True)
+    O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
+    torch.cuda.synchronize()
+    assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
