@@ -28,10 +28,19 @@ order; a key is visible to a query when its global position is <= the query's;
 the scale is 1/sqrt(D); dropout is off; a query row with no visible key gives
 O = 0 and lse = -inf; lse is a natural logarithm.
 
+Rotary position embedding (rope, permute_to_ranks_rope) follows the same
+page's 工程实践 rule that positions are global, with the frequency schedule of
+the sinusoidal table in "Tensor并行与算子拆分" (model code, PositionalEncoding);
+the rotation itself is the standard rotary embedding (the pages give no
+formula for it).
+
 Pins (tests/test_oracle_pins.py): a pure-Python triple loop, torch's
 scaled_dot_product_attention in float64, closed forms (uniform scores,
 constant V, first causal row), the chunk-then-merge invariant of the pages,
-merge algebra, structural invariants and the zigzag balance count.  Every
+merge algebra, structural invariants and the zigzag balance count; for rope
+the pages' sinusoidal table itself, pair-norm preservation, the identity at
+position 0, the dependence of q.k on the position difference only, and the
+global-versus-local position check.  Every
 function below is pinned; none is "parity unpinned".
 """
 from __future__ import annotations
@@ -112,6 +121,64 @@ def permute_from_ranks(y: np.ndarray, pos: np.ndarray, L: int) -> np.ndarray:
     for r in range(N):
         out[:, :, pos[r]] = y[r]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding at global positions
+# ---------------------------------------------------------------------------
+
+ROPE_INTERLEAVED = 0  # pairs (2k, 2k+1)
+ROPE_HALF = 1         # pairs (k, k + D/2)
+
+
+def rope_frequencies(D: int, base: float = 10000.0) -> np.ndarray:
+    """theta_k = base^(-2k/D), k = 0 .. D/2-1: the frequency schedule of the
+    sinusoidal table in "Tensor并行与算子拆分" (model code, PositionalEncoding:
+    the divisor term is exp(-2k ln(10000) / d_model))."""
+    k = np.arange(D // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * k / D)
+
+
+def rope_pairs(D: int, pairing: int) -> tuple[np.ndarray, np.ndarray]:
+    """Indices (a_k, b_k) of the two elements rotated together by theta_k."""
+    k = np.arange(D // 2)
+    if pairing == ROPE_INTERLEAVED:
+        return 2 * k, 2 * k + 1
+    if pairing == ROPE_HALF:
+        return k, k + D // 2
+    raise ValueError(pairing)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float = 10000.0,
+         pairing: int = ROPE_INTERLEAVED) -> np.ndarray:
+    """Rotate every row of x [..., rows, D] by its position: for each pair
+    (a_k, b_k) and angle phi = pos * theta_k,
+        y[a_k] = x[a_k] cos(phi) - x[b_k] sin(phi)
+        y[b_k] = x[a_k] sin(phi) + x[b_k] cos(phi).
+    `pos` [rows] are GLOBAL token positions: under CP every rank rotates its
+    tokens by their place in the whole sequence, not by their local index
+    ("序列与上下文并行", 工程实践: position encodings use the global offset of
+    each rank's segment).  Reading: rotary embedding on the pages' sinusoidal
+    frequency schedule; float64 throughout."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if D % 2:
+        raise ValueError("rope needs an even head dimension")
+    a, b = rope_pairs(D, pairing)
+    phi = np.asarray(pos, dtype=np.float64)[:, None] * rope_frequencies(D, base)[None, :]
+    c, s = np.cos(phi), np.sin(phi)
+    y = np.empty_like(x)
+    y[..., a] = x[..., a] * c - x[..., b] * s
+    y[..., b] = x[..., a] * s + x[..., b] * c
+    return y
+
+
+def permute_to_ranks_rope(x: np.ndarray, pos: np.ndarray, base: float = 10000.0,
+                          pairing: int = ROPE_INTERLEAVED) -> np.ndarray:
+    """Rank-major rows of x, each rotated at its global position:
+    out[r, b, h, t] = rope(x[b, h, pos[r, t]], pos[r, t])."""
+    return np.stack([rope(x[:, :, pos[r]], pos[r], base, pairing) for r in range(pos.shape[0])],
+                    axis=0)
 
 
 # ---------------------------------------------------------------------------

@@ -248,10 +248,96 @@ def check_sampled_rows(orc):
     assert np.max(np.abs(Or - O[0, 0, rows])) <= TOL and np.max(np.abs(lser - lse[0, 0, rows])) <= TOL
 
 
+# ------------------------------------------------------------------ rope pins
+
+def _page_sinusoid(p, d):
+    """The sinusoidal table of "Tensor并行与算子拆分" (model code,
+    PositionalEncoding), written out with the page's own steps: divisor
+    exp(2k * (-ln 10000 / d)); even columns sin(p * div), odd columns cos."""
+    row = [0.0] * d
+    for k2 in range(0, d, 2):
+        div = math.exp(k2 * (-math.log(10000.0) / d))
+        row[k2] = math.sin(p * div)
+        row[k2 + 1] = math.cos(p * div)
+    return row
+
+
+def check_rope_sinusoid_table(orc):
+    """Rotating the unit vector (1, 0) of every pair by position p gives
+    (cos, sin) of the pages' table at p: this fixes the frequency schedule,
+    the pairing and the direction of the rotation."""
+    for d in (2, 8, 16, 128):
+        positions = np.array([0, 1, 2, 7, 100, 4095, 131071], dtype=np.int64)
+        table = np.array([_page_sinusoid(int(p), d) for p in positions])
+        for pairing in (orc.ROPE_INTERLEAVED, orc.ROPE_HALF):
+            x = np.zeros((len(positions), d))
+            first = np.arange(0, d, 2) if pairing == orc.ROPE_INTERLEAVED else np.arange(d // 2)
+            second = first + 1 if pairing == orc.ROPE_INTERLEAVED else first + d // 2
+            x[:, first] = 1.0
+            y = orc.rope(x, positions, 10000.0, pairing)
+            # large angles: allow for the rounding of p * theta (|angle| <= 1.4e5)
+            assert np.max(np.abs(y[:, first] - table[:, 1::2])) < 1e-9
+            assert np.max(np.abs(y[:, second] - table[:, 0::2])) < 1e-9
+
+
+def check_rope_norm_and_identity(orc):
+    """A rotation keeps every pair's length; position 0 is the identity."""
+    x = _rand((3, 40, 64), 11)
+    pos = np.arange(1000, 1040, dtype=np.int64)
+    for pairing in (orc.ROPE_INTERLEAVED, orc.ROPE_HALF):
+        y = orc.rope(x, pos, 10000.0, pairing)
+        a, b = orc.rope_pairs(64, pairing)
+        assert np.allclose(y[..., a] ** 2 + y[..., b] ** 2, x[..., a] ** 2 + x[..., b] ** 2,
+                           rtol=1e-12, atol=1e-12)
+        assert not np.allclose(y, x)
+        assert np.array_equal(orc.rope(x, np.zeros(40, dtype=np.int64), 10000.0, pairing), x)
+
+
+def check_rope_relative(orc):
+    """q.k after rotation depends on the position difference only, through the
+    closed form sum_k [(qa ka + qb kb) cos(dn theta_k) + (qb ka - qa kb) sin(dn theta_k)],
+    dn = n - m (rotary embedding's defining property)."""
+    D = 32
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    theta = np.array([10000.0 ** (-2.0 * j / D) for j in range(D // 2)])
+    for pairing in (orc.ROPE_INTERLEAVED, orc.ROPE_HALF):
+        a, b = (np.arange(0, D, 2), np.arange(1, D, 2)) if pairing == orc.ROPE_INTERLEAVED else \
+            (np.arange(D // 2), np.arange(D // 2, D))
+        for m, n in [(0, 0), (3, 10), (10, 3), (500, 77), (65536, 65535)]:
+            qm = orc.rope(q[None], np.array([m]), 10000.0, pairing)[0]
+            kn = orc.rope(k[None], np.array([n]), 10000.0, pairing)[0]
+            dn = n - m
+            want = np.sum((q[a] * k[a] + q[b] * k[b]) * np.cos(dn * theta)
+                          + (q[b] * k[a] - q[a] * k[b]) * np.sin(dn * theta))
+            assert abs(qm @ kn - want) < 1e-9 * (1 + abs(want)), (pairing, m, n)
+
+
+def check_rope_global_positions(orc):
+    """Rank-major rotated rows equal the globally rotated sequence, gathered by
+    the layout; rotating by local indices instead (the offset bug the pages
+    warn of) changes every rank but rank 0's first chunk."""
+    L, N, D = 64, 4, 16
+    x = _rand((2, 3, L, D), 12)
+    pos = orc.zigzag_layout(L, N)
+    for pairing in (orc.ROPE_INTERLEAVED, orc.ROPE_HALF):
+        got = orc.permute_to_ranks_rope(x, pos, 10000.0, pairing)
+        want = orc.permute_to_ranks(orc.rope(x, np.arange(L), 10000.0, pairing), pos)
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+        local = np.stack([orc.rope(x[:, :, pos[r]], np.arange(L // N), 10000.0, pairing)
+                          for r in range(N)])
+        C = L // (2 * N)
+        assert np.allclose(local[0, :, :, :C], got[0, :, :, :C])
+        assert not np.allclose(local[0, :, :, C:], got[0, :, :, C:])
+        for r in range(1, N):
+            assert not np.allclose(local[r], got[r])
+
+
 PINS = [check_layout_golden, check_layout_permutation, check_layout_balance, check_ring_order,
         check_permute, check_brute_force, check_sdpa, check_uniform_scores,
         check_constant_v_and_first_row, check_chunk_merge_invariant, check_partial_empty_rows,
-        check_merge_algebra, check_structural, check_sampled_rows]
+        check_merge_algebra, check_structural, check_sampled_rows, check_rope_sinusoid_table,
+        check_rope_norm_and_identity, check_rope_relative, check_rope_global_positions]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -297,6 +383,15 @@ MUTANTS = {
     "empty row lse": ("lse = np.full(q.shape[0], NEG_INF, dtype=np.float64)",
                       "lse = np.full(q.shape[0], 0.0, dtype=np.float64)"),
     "pair count": ("side=\"right\"", "side=\"left\""),
+    "rope sin sign": ("y[..., a] = x[..., a] * c - x[..., b] * s",
+                      "y[..., a] = x[..., a] * c + x[..., b] * s"),
+    "rope frequency": ("np.power(float(base), -2.0 * k / D)", "np.power(float(base), -1.0 * k / D)"),
+    "rope pairing": ("return 2 * k, 2 * k + 1", "return 2 * k + 1, 2 * k"),
+    "rope half pairing": ("return k, k + D // 2", "return k, D - 1 - k"),
+    "rope local positions": ("rope(x[:, :, pos[r]], pos[r], base, pairing)",
+                             "rope(x[:, :, pos[r]], np.arange(pos.shape[1]), base, pairing)"),
+    "rope position offset": ("phi = np.asarray(pos, dtype=np.float64)[:, None]",
+                             "phi = (np.asarray(pos, dtype=np.float64)[:, None] + 1)"),
 }
 
 
