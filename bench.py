@@ -209,6 +209,7 @@ def main():
                 lse=tl), 1)]
     mevs = timed(lambda: cpa.merge(pipe.Or[0], pipe.lser[0], tO, tl), reps)
     pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr), reps)
+    rope_evs = timed(lambda: cpa.zigzag_permute_rope(K, pos_d, w.N, 10000.0, out=pipe.Kr), reps)
     torch.cuda.synchronize()
     p_ms = np.array([a.elapsed_time(b) for _, (a, b) in part_evs])
     p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _ in part_evs])
@@ -227,6 +228,7 @@ def main():
     m_bytes = w.B * w.H * Lr * (w.D + 1) * 4 * 3  # read acc + new, write acc (O and lse)
     perm_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
     perm_bytes = 2 * K.numel() * K.element_size()
+    rope_ms = float(np.mean([a.elapsed_time(b) for a, b in rope_evs]))
 
     value = useful / (ms_step * 1e-3) / 1e12
     out = {
@@ -262,6 +264,9 @@ def main():
             "permute_K": {"ms": round(perm_ms, 4),
                           "GB/s": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
                           "bytes": perm_bytes},
+            "permute_rope_K": {"ms": round(rope_ms, 4),
+                               "GB/s": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
+                               "bytes": perm_bytes},
             "ms_per_step_events": round(ms_step_ev, 4),
         },
         "cpu_baseline": None,

@@ -128,12 +128,15 @@ cpa_status cpa_rank_forward(int32_t i, int32_t N, const void *Q_i, const void *K
                             size_t ws_bytes, void *stream);
 
 /*
- * Rank i's whole ring in ONE launch: the same result as cpa_rank_forward, but
- * the kernel walks the N K/V blocks itself in ring order j = i, i+1, ...
- * (mod N) and keeps the online-softmax state (O, running max, sums) in
- * registers from one block to the next ("序列与上下文并行", 上下文并行: the
- * partial results are folded incrementally), so no partial O is written and
- * no merge pass runs.  Arguments as for cpa_rank_forward, without workspace.
+ * Rank i's whole ring in ONE launch: the same result as cpa_rank_forward (up
+ * to rounding order), but the kernel walks the N K/V blocks itself and keeps
+ * the online-softmax state (O, running max, sums) in registers from one block
+ * to the next ("序列与上下文并行", 上下文并行: the partial results are folded
+ * incrementally), so no partial O is written and no merge pass runs.  The
+ * blocks are visited as j = i+1, i+2, ..., i+N-1, i (mod N): the rank's own
+ * block comes last, which keeps the workgroups of a head in step through the
+ * other blocks (better L2 reuse); the result does not depend on the order
+ * beyond rounding.  Arguments as for cpa_rank_forward, without workspace.
  * bf16 with D = 64 or 128 only (CPA_EUNSUPPORTED otherwise; use
  * cpa_rank_forward for fp32 or D = 16).
  */
@@ -160,11 +163,50 @@ cpa_status cpa_zigzag_permute(const void *src, void *dst, int32_t elem_bytes,
                               const int64_t *pos_all, int32_t N, int32_t rank_lo,
                               int32_t rank_hi, int32_t inverse, void *stream);
 
+/* Pairing of the elements a rotary embedding rotates together. */
+typedef enum {
+  CPA_ROPE_INTERLEAVED = 0, /* pairs (2k, 2k+1), as the sinusoidal table interleaves sin/cos */
+  CPA_ROPE_HALF = 1         /* pairs (k, k + D/2) */
+} cpa_rope_pairing;
+
+/*
+ * Rotary position embedding at GLOBAL positions ("序列与上下文并行", 工程实践:
+ * after the CP split, positions are global, so each rank must know the global
+ * offset of its segment).  Frequencies theta_k = base^(-2k/D), k < D/2, the
+ * schedule of the sinusoidal table in "Tensor并行与算子拆分" (model code,
+ * PositionalEncoding).  Pair k = (a, b) of a row at position p is rotated by
+ * phi = p * theta_k:  y_a = x_a cos phi - x_b sin phi,  y_b = x_a sin phi + x_b cos phi.
+ * The angle is reduced in float64 before a float32 sin/cos, so it stays
+ * accurate at million-token positions; the rotation is float32 and bf16
+ * results are rounded to nearest even.
+ *   x, y     device [B, H, rows, D] of `dt` (y may equal x: in place)
+ *   pos      device int64 [rows]: global position of each row (any order, >= 0)
+ *   base     > 1 (10000 in the pages' table)
+ *   pairing  cpa_rope_pairing
+ * D must be a multiple of 8 in [8, 512] (CPA_EUNSUPPORTED otherwise).
+ */
+cpa_status cpa_rope(const void *x, void *y, cpa_dtype dt, int32_t B, int32_t H, int64_t rows,
+                    int32_t D, const int64_t *pos, double base, int32_t pairing, void *stream);
+
+/*
+ * cpa_zigzag_permute (forward) with the rotary embedding folded in: one pass
+ * over memory that gathers each rank's rows and rotates each at its global
+ * position,
+ *   dst[r - rank_lo, b, h, t, :] = rope(src[b, h, pos_all[r, t], :], pos_all[r, t]).
+ * Arguments as for cpa_zigzag_permute (src global [B, H, L, D], dst rank-major
+ * [rank_hi - rank_lo, B, H, L/N, D], both of `dt`; src and dst must not
+ * overlap) and cpa_rope (base, pairing, D).
+ */
+cpa_status cpa_zigzag_permute_rope(const void *src, void *dst, cpa_dtype dt, int32_t B,
+                                   int32_t H, int64_t L, int32_t D, const int64_t *pos_all,
+                                   int32_t N, int32_t rank_lo, int32_t rank_hi, double base,
+                                   int32_t pairing, void *stream);
+
 /* Text of the last error on the calling thread ("" if none); valid until the
  * thread's next call into the library. */
 const char *cpa_last_error(void);
 
-/* Library version, e.g. "libcpattn 0.1.0 gfx950". */
+/* Library version, e.g. "libcpattn 0.2.0 gfx950". */
 const char *cpa_version(void);
 
 #ifdef __cplusplus

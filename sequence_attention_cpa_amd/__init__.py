@@ -8,11 +8,12 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (CPA_BF16, CPA_F32, CpaError, check, last_error, load,  # noqa: F401
-                   version)
+from ._lib import (CPA_BF16, CPA_F32, CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED,  # noqa: F401
+                   CpaError, check, last_error, load, version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
-           "rank_forward_fused", "zigzag_permute", "last_error", "version", "CpaError"]
+           "rank_forward_fused", "zigzag_permute", "rope", "zigzag_permute_rope", "last_error",
+           "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
 
 
 def _torch():
@@ -152,4 +153,34 @@ def zigzag_permute(src, pos_all, N: int, inverse: bool = False, rank_lo: int = 0
     check(load().cpa_zigzag_permute(_ptr(src), _ptr(out), src.element_size(), B, H, L, D,
                                     _ptr(pos_all), N, rank_lo, rank_hi, int(bool(inverse)),
                                     _stream(src)))
+    return out
+
+
+def rope(x, pos, base: float = 10000.0, pairing: int = CPA_ROPE_INTERLEAVED, out=None):
+    """Rotary embedding of x [B,H,rows,D] at global positions pos [rows]
+    (out=x rotates in place)."""
+    torch = _torch()
+    B, H, rows, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _need_gpu(x, pos, out)
+    check(load().cpa_rope(_ptr(x), _ptr(out), _dtype_code(x), B, H, rows, D, _ptr(pos),
+                          float(base), int(pairing), _stream(x)))
+    return out
+
+
+def zigzag_permute_rope(src, pos_all, N: int, base: float = 10000.0,
+                        pairing: int = CPA_ROPE_INTERLEAVED, rank_lo: int = 0,
+                        rank_hi: int | None = None, out=None):
+    """Global [B,H,L,D] -> rank-major [nr,B,H,L/N,D], each row rotated at its
+    global position (the forward permute with the rotary embedding folded in)."""
+    torch = _torch()
+    rank_hi = N if rank_hi is None else rank_hi
+    B, H, L, D = src.shape
+    if out is None:
+        out = torch.empty((rank_hi - rank_lo, B, H, L // N, D), dtype=src.dtype, device=src.device)
+    _need_gpu(src, pos_all, out)
+    check(load().cpa_zigzag_permute_rope(_ptr(src), _ptr(out), _dtype_code(src), B, H, L, D,
+                                         _ptr(pos_all), N, rank_lo, rank_hi, float(base),
+                                         int(pairing), _stream(src)))
     return out

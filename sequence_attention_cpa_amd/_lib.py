@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libcpattn.so")
 
 CPA_OK, CPA_EINVAL, CPA_ESHAPE, CPA_EDTYPE, CPA_EUNSUPPORTED, CPA_EHIP = range(6)
 CPA_BF16, CPA_F32 = 0, 1
+CPA_ROPE_INTERLEAVED, CPA_ROPE_HALF = 0, 1
 STATUS_NAMES = {0: "CPA_OK", 1: "CPA_EINVAL", 2: "CPA_ESHAPE", 3: "CPA_EDTYPE",
                 4: "CPA_EUNSUPPORTED", 5: "CPA_EHIP"}
 
@@ -21,6 +22,7 @@ STATUS_NAMES = {0: "CPA_OK", 1: "CPA_EINVAL", 2: "CPA_ESHAPE", 3: "CPA_EDTYPE",
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
 _i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_f64 = ctypes.c_double
 SIGNATURES = {
     "cpa_zigzag_layout": (ctypes.c_int, [_i64, _i32, _c_i64p]),
     "cpa_partial": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i64, _i32,
@@ -33,6 +35,10 @@ SIGNATURES = {
                                               _i32, _i64, _i32, _i32, _f32, _vp, _vp, _vp]),
     "cpa_zigzag_permute": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _i32,
                                           _i32, _i32, _i32, _vp]),
+    "cpa_rope": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32, _vp, _f64, _i32,
+                                _vp]),
+    "cpa_zigzag_permute_rope": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32, _vp,
+                                               _i32, _i32, _i32, _f64, _i32, _vp]),
     "cpa_last_error": (ctypes.c_char_p, []),
     "cpa_version": (ctypes.c_char_p, []),
 }

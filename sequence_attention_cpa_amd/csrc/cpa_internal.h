@@ -15,8 +15,8 @@ hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V,
                                float scale, hipStream_t stream);
 
 // Rank i's whole ring in one launch: Q_i [BH, Lr, D] against the N blocks of
-// rank-major K_all / V_all [N, BH, Lr, D] (positions pos_all [N, Lr]) in ring
-// order i, i+1, ..., online-softmax state kept in registers (D = 64 or 128).
+// rank-major K_all / V_all [N, BH, Lr, D] (positions pos_all [N, Lr]) in the
+// order i+1, ..., i+N-1, i, online-softmax state kept in registers (D = 64 or 128).
 hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_all,
                             const int64_t* q_off, const int64_t* pos_all, float* O, float* lse,
                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
@@ -37,5 +37,13 @@ hipError_t launch_merge(float* O_acc, float* lse_acc, const float* O_new, const 
 hipError_t launch_permute(const void* src, void* dst, int64_t row_bytes, int64_t BH, int64_t L,
                           const int64_t* pos_all, int N, int rank_lo, int rank_hi, bool inverse,
                           hipStream_t stream);
+
+// Rotary position embedding of rows at given global positions (D % 8 == 0).
+// Index space: nr x Lr positions pos[rr*Lr + t]; destination rows
+// (rr*BH + bh)*Lr + t of [nr, BH, Lr, D]; source rows bh*L + p of global
+// [BH, L, D] when `gather`, else the destination's own layout (may alias dst).
+hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t BH, int64_t L, int64_t Lr,
+                       int64_t nr, int D, const int64_t* pos, bool gather, double base, bool half,
+                       hipStream_t stream);
 
 }  // namespace cpa

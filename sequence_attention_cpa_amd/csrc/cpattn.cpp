@@ -92,13 +92,27 @@ cpa_status check_rank_shape(int32_t N, int64_t L, int32_t B, int32_t H, int32_t 
   return CPA_OK;
 }
 
+cpa_status check_rope(cpa_dtype dt, int32_t B, int32_t H, int32_t D, double base,
+                      int32_t pairing) {
+  if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
+  if (B < 1 || H < 1) return fail(CPA_ESHAPE, "B and H must be >= 1 (B=%d, H=%d)", B, H);
+  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if (D < 8 || D > 512 || D % 8 != 0)
+    return fail(CPA_EUNSUPPORTED, "rope needs D a multiple of 8 in [8, 512] (D=%d)", D);
+  if (!(base > 1.0) || !std::isfinite(base))
+    return fail(CPA_EINVAL, "rope base must be finite and > 1 (base=%g)", base);
+  if (pairing != CPA_ROPE_INTERLEAVED && pairing != CPA_ROPE_HALF)
+    return fail(CPA_EINVAL, "unknown rope pairing %d", pairing);
+  return CPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* cpa_last_error(void) { return g_err.c_str(); }
 
-const char* cpa_version(void) { return "libcpattn 0.1.0 gfx950"; }
+const char* cpa_version(void) { return "libcpattn 0.2.0 gfx950"; }
 
 cpa_status cpa_zigzag_layout(int64_t L, int32_t N, int64_t* out) {
   if (N < 1) return fail(CPA_EINVAL, "N must be >= 1 (N=%d)", N);
@@ -231,6 +245,40 @@ cpa_status cpa_zigzag_permute(const void* src, void* dst, int32_t elem_bytes, in
   return from_hip(cpa::launch_permute(src, dst, row_bytes, (int64_t)B * H, L, pos_all, N, rank_lo,
                                       rank_hi, inverse != 0, (hipStream_t)stream),
                   "permute launch");
+}
+
+cpa_status cpa_rope(const void* x, void* y, cpa_dtype dt, int32_t B, int32_t H, int64_t rows,
+                    int32_t D, const int64_t* pos, double base, int32_t pairing, void* stream) {
+  cpa_status st = check_rope(dt, B, H, D, base, pairing);
+  if (st != CPA_OK) return st;
+  if (rows < 0) return fail(CPA_ESHAPE, "rows must be >= 0 (rows=%lld)", (long long)rows);
+  if (rows == 0) return ok();
+  if (!x || !y || !pos) return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(CPA_EINVAL, "x/y must be 16-byte aligned");
+  if (!aligned(pos, 8)) return fail(CPA_EINVAL, "pos must be 8-byte aligned");
+  return from_hip(cpa::launch_rope(x, y, dt == CPA_BF16, (int64_t)B * H, rows, rows, 1, D, pos,
+                                   false, base, pairing == CPA_ROPE_HALF, (hipStream_t)stream),
+                  "rope launch");
+}
+
+cpa_status cpa_zigzag_permute_rope(const void* src, void* dst, cpa_dtype dt, int32_t B, int32_t H,
+                                   int64_t L, int32_t D, const int64_t* pos_all, int32_t N,
+                                   int32_t rank_lo, int32_t rank_hi, double base, int32_t pairing,
+                                   void* stream) {
+  cpa_status st = check_rope(dt, B, H, D, base, pairing);
+  if (st != CPA_OK) return st;
+  st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (rank_lo < 0 || rank_hi > N || rank_lo >= rank_hi)
+    return fail(CPA_EINVAL, "rank range [%d, %d) invalid for N=%d", rank_lo, rank_hi, N);
+  if (!src || !dst || !pos_all) return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(CPA_EINVAL, "src/dst must be 16-byte aligned");
+  if (!aligned(pos_all, 8)) return fail(CPA_EINVAL, "pos_all must be 8-byte aligned");
+  const int64_t Lr = L / N;
+  return from_hip(cpa::launch_rope(src, dst, dt == CPA_BF16, (int64_t)B * H, L, Lr,
+                                   rank_hi - rank_lo, D, pos_all + (int64_t)rank_lo * Lr, true,
+                                   base, pairing == CPA_ROPE_HALF, (hipStream_t)stream),
+                  "permute+rope launch");
 }
 
 }  // extern "C"

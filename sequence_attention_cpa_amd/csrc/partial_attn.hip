@@ -146,9 +146,15 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32
 
 // Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
 // K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
-// the order b = first, first + 1, ... (mod nblk).  One block is one ring step
-// (cpa_partial); nblk = N with first = i is rank i's whole ring, the running
-// (O, max, sums) staying in registers from one block to the next.
+// the order b = first + 1, first + 2, ..., first (mod nblk).  One block is one
+// ring step (cpa_partial); nblk = N with first = i is rank i's whole ring, the
+// running (O, max, sums) staying in registers from one block to the next.
+// Visiting the rank's own block last is deliberate: in every other block a
+// query tile sees either none of the keys or the same whole prefix as its
+// neighbours (the zigzag chunks do not interleave), so the workgroups of a
+// head sweep those blocks in step and share each K/V tile through L2; only
+// the own block gives every tile a different causal prefix, after which the
+// workgroups no longer run in step.
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   using BF = std::false_type;
 
   for (int sb = 0; sb < nblk; ++sb) {
-  const int blk = (first + sb) % nblk;
+  const int blk = (first + 1 + sb) % nblk;
   Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
   Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
   if (causal) {

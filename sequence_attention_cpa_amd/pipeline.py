@@ -11,22 +11,28 @@ With `fused=True` each rank's ring is one launch (cpa_rank_forward_fused:
 the online-softmax state stays in registers across the N blocks) instead of
 N partial launches and N-1 merges; bf16 with D = 64 or 128 only.
 
+With `rope_base` set, Q and K are rotated at their global positions on the
+way into rank-major order (cpa_zigzag_permute_rope: the rotary embedding is
+folded into the permute, so it costs no extra pass over memory).
+
 All buffers are allocated once in the constructor; `step` allocates nothing.
 """
 from __future__ import annotations
 
-from . import (rank_forward, rank_forward_fused, rank_forward_workspace, zigzag_layout,
-               zigzag_permute)
+from . import (CPA_ROPE_INTERLEAVED, rank_forward, rank_forward_fused, rank_forward_workspace,
+               zigzag_layout, zigzag_permute, zigzag_permute_rope)
 
 
 class SharePipeline:
     def __init__(self, B: int, H: int, L: int, D: int, N: int, causal: bool, dtype, device,
                  rank_lo: int = 0, rank_hi: int | None = None, scale: float = 0.0,
-                 fused: bool = False):
+                 fused: bool = False, rope_base: float | None = None,
+                 rope_pairing: int = CPA_ROPE_INTERLEAVED):
         import torch
 
         self.B, self.H, self.L, self.D, self.N = B, H, L, D, N
         self.causal, self.scale, self.fused = causal, scale, fused
+        self.rope_base, self.rope_pairing = rope_base, rope_pairing
         self.rank_lo = rank_lo
         self.rank_hi = N if rank_hi is None else rank_hi
         nr = self.rank_hi - self.rank_lo
@@ -47,9 +53,14 @@ class SharePipeline:
         """Q, K, V: global [B, H, L, D] on the device.  Returns global (O, lse);
         rows of ranks outside [rank_lo, rank_hi) are left as initialised."""
         N, lo, hi = self.N, self.rank_lo, self.rank_hi
-        zigzag_permute(K, self.pos, N, out=self.Kr)
+        if self.rope_base is None:
+            zigzag_permute(K, self.pos, N, out=self.Kr)
+            zigzag_permute(Q, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Qr)
+        else:
+            zigzag_permute_rope(K, self.pos, N, self.rope_base, self.rope_pairing, out=self.Kr)
+            zigzag_permute_rope(Q, self.pos, N, self.rope_base, self.rope_pairing, rank_lo=lo,
+                                rank_hi=hi, out=self.Qr)
         zigzag_permute(V, self.pos, N, out=self.Vr)
-        zigzag_permute(Q, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Qr)
         self.ring()
         zigzag_permute(self.Or, self.pos, N, inverse=True, rank_lo=lo, rank_hi=hi, out=self.O)
         zigzag_permute(self.lser, self.pos, N, inverse=True, rank_lo=lo, rank_hi=hi, out=self.lse)

@@ -221,3 +221,62 @@ def test_binding_rejects_cpu_tensors(lib):
     pos = torch.zeros(64, dtype=torch.int64)
     with pytest.raises(cpa.CpaError):
         cpa.partial(x, x, x, pos, pos, True)
+
+
+def _rope(lib, **kw):
+    a = dict(x=P, y=P, dt=_lib.CPA_BF16, B=1, H=2, rows=64, D=128, pos=P, base=10000.0,
+             pairing=0, stream=None)
+    a.update(kw)
+    return lib.cpa_rope(a["x"], a["y"], a["dt"], a["B"], a["H"], a["rows"], a["D"], a["pos"],
+                        a["base"], a["pairing"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=9), _lib.CPA_EDTYPE),
+    (dict(B=0), _lib.CPA_ESHAPE),
+    (dict(rows=-1), _lib.CPA_ESHAPE),
+    (dict(D=12), _lib.CPA_EUNSUPPORTED),
+    (dict(D=4), _lib.CPA_EUNSUPPORTED),
+    (dict(D=520), _lib.CPA_EUNSUPPORTED),
+    (dict(base=1.0), _lib.CPA_EINVAL),
+    (dict(base=float("nan")), _lib.CPA_EINVAL),
+    (dict(base=float("inf")), _lib.CPA_EINVAL),
+    (dict(pairing=2), _lib.CPA_EINVAL),
+    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(y=None), _lib.CPA_EINVAL),
+    (dict(x=P + 8), _lib.CPA_EINVAL),
+    (dict(pos=P + 4), _lib.CPA_EINVAL),
+])
+def test_rope_rejects(lib, kw, status):
+    assert _rope(lib, **kw) == status
+    assert cpa.last_error() != ""
+
+
+def test_rope_zero_rows_is_a_no_op(lib):
+    assert _rope(lib, rows=0, x=None, y=None, pos=None) == _lib.CPA_OK
+
+
+def _perm_rope(lib, **kw):
+    a = dict(src=P, dst=P + 4096, dt=_lib.CPA_BF16, B=1, H=2, L=256, D=128, pos=P, N=4, lo=0, hi=4,
+             base=10000.0, pairing=1, stream=None)
+    a.update(kw)
+    return lib.cpa_zigzag_permute_rope(a["src"], a["dst"], a["dt"], a["B"], a["H"], a["L"], a["D"],
+                                       a["pos"], a["N"], a["lo"], a["hi"], a["base"], a["pairing"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=250), _lib.CPA_ESHAPE),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(lo=3, hi=2), _lib.CPA_EINVAL),
+    (dict(hi=5), _lib.CPA_EINVAL),
+    (dict(D=20), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=3), _lib.CPA_EDTYPE),
+    (dict(base=0.5), _lib.CPA_EINVAL),
+    (dict(pairing=-1), _lib.CPA_EINVAL),
+    (dict(src=None), _lib.CPA_EINVAL),
+    (dict(dst=P + 8), _lib.CPA_EINVAL),
+])
+def test_permute_rope_rejects(lib, kw, status):
+    assert _perm_rope(lib, **kw) == status
+    assert cpa.last_error() != ""
