@@ -34,13 +34,19 @@ the sinusoidal table in "Tensor并行与算子拆分" (model code, PositionalEnc
 the rotation itself is the standard rotary embedding (the pages give no
 formula for it).
 
+The backward (backward_block and the functions built on it) is the
+derivative of the same attention, written out; the pages state only that CP
+is validated on training losses (the same page, 工程实践).
+
 Pins (tests/test_oracle_pins.py): a pure-Python triple loop, torch's
 scaled_dot_product_attention in float64, closed forms (uniform scores,
 constant V, first causal row), the chunk-then-merge invariant of the pages,
 merge algebra, structural invariants and the zigzag balance count; for rope
 the pages' sinusoidal table itself, pair-norm preservation, the identity at
 position 0, the dependence of q.k on the position difference only, and the
-global-versus-local position check.  Every
+global-versus-local position check; for the backward torch autograd in
+float64, central finite differences, the block-by-block ring decomposition,
+the zero sum of dK over keys, the sum of dV over keys and constant V.  Every
 function below is pinned; none is "parity unpinned".
 """
 from __future__ import annotations
@@ -330,6 +336,124 @@ def rank_forward(i: int, Q_i: np.ndarray, K_ranks: np.ndarray, V_ranks: np.ndarr
         else:
             O, lse = merge(O, lse, O_s, lse_s)
     return O, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward: gradients of the attention output
+# ---------------------------------------------------------------------------
+#
+# The pages give no backward; CP exists for training ("序列与上下文并行": the
+# numerical check of CP compares training losses, 工程实践), so the gradients
+# are needed.  They are the derivative of O = softmax(s) v, s = q k^T * scale
+# + mask, for an upstream gradient dO:
+#     P = exp(s - lse) on visible pairs, 0 elsewhere   (the forward's weights)
+#     dP = dO v^T,  delta_t = sum_u P[t, u] dP[t, u] = sum_d dO[t, d] O[t, d]
+#     dS = P * (dP - delta)   (derivative of the softmax)
+#     dq = scale * dS k,  dk = scale * dS^T q,  dv = P^T dO.
+# Under CP the same formulas hold block by block when P uses the query row's
+# FINAL lse over all its keys, so rank i's gradient contributions against
+# K/V block j need only (Q_i, dO_i, lse_i, delta_i) and (K_j, V_j).
+
+def backward_delta(O: np.ndarray, dO: np.ndarray) -> np.ndarray:
+    """delta [..., rows] = sum over d of dO * O (equal to sum_u P dP)."""
+    return np.sum(np.asarray(dO, dtype=np.float64) * np.asarray(O, dtype=np.float64), axis=-1)
+
+
+def backward_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, dO: np.ndarray,
+                   lse: np.ndarray, delta: np.ndarray, q_pos: np.ndarray, k_pos: np.ndarray,
+                   causal: bool, scale: float | None = None):
+    """Gradient contributions of one query block against one key/value block
+    of one (batch, head), given the query rows' final lse and delta.
+    Returns (dq [Lq, D], dk [Lk, D], dv [Lk, D]).  Rows with lse = -inf (no
+    visible key anywhere) contribute nothing."""
+    D = q.shape[1]
+    if scale is None:
+        scale = default_scale(D)
+    s = scale * (q @ k.T)
+    fin = np.isfinite(lse)
+    ok = visible(q_pos, k_pos, causal) & fin[:, None]
+    P = np.zeros_like(s)
+    P[ok] = np.exp(s - np.where(fin, lse, 0.0)[:, None])[ok]
+    dP = dO @ v.T
+    dS = P * (dP - delta[:, None])
+    return scale * (dS @ k), scale * (dS.T @ q), P.T @ dO
+
+
+def backward_rows(q_rows: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndarray,
+                  dO_rows: np.ndarray, lse_rows: np.ndarray, delta_rows: np.ndarray,
+                  causal: bool, scale: float | None = None, block: int = 256):
+    """backward_block of selected query rows of one (batch, head) against the
+    whole sequence (key u at position u), `block` rows at a time.  Returns dq
+    of those rows and their summed contributions to dk, dv [L, D]."""
+    L, D = k.shape
+    dq = np.empty((q_rows.shape[0], D), dtype=np.float64)
+    dk = np.zeros((L, D), dtype=np.float64)
+    dv = np.zeros((L, v.shape[1]), dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    for a in range(0, q_rows.shape[0], block):
+        b = min(a + block, q_rows.shape[0])
+        kend = (int(q_pos[a:b].max()) + 1) if causal else L
+        dq[a:b], dk_b, dv_b = backward_block(q_rows[a:b], k[:kend], v[:kend], dO_rows[a:b],
+                                             lse_rows[a:b], delta_rows[a:b], q_pos[a:b],
+                                             np.arange(kend, dtype=np.int64), causal, scale)
+        dk[:kend] += dk_b
+        dv[:kend] += dv_b
+    return dq, dk, dv
+
+
+def attention_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray,
+                       causal: bool, scale: float | None = None):
+    """Gradients of sum(dO * O) with respect to Q, K, V of whole-sequence
+    attention, all [B, H, L, D] float64."""
+    O, lse = attention(Q, K, V, causal, scale)
+    delta = backward_delta(O, dO)
+    B, H, L, _ = Q.shape
+    pos = np.arange(L, dtype=np.int64)
+    dQ, dK, dV = np.empty_like(Q), np.empty_like(K), np.empty_like(V)
+    for b in range(B):
+        for h in range(H):
+            dQ[b, h], dK[b, h], dV[b, h] = backward_rows(Q[b, h], pos, K[b, h], V[b, h],
+                                                         dO[b, h], lse[b, h], delta[b, h],
+                                                         causal, scale)
+    return dQ, dK, dV
+
+
+def partial_backward(Qi: np.ndarray, Kj: np.ndarray, Vj: np.ndarray, dOi: np.ndarray,
+                     lse_i: np.ndarray, delta_i: np.ndarray, q_off: np.ndarray,
+                     k_off: np.ndarray, causal: bool, scale: float | None = None):
+    """One ring step of the backward: rank i's (Q, dO, lse, delta) against
+    rank j's K/V, [B, H, rows, D].  Returns (dQ_ij, dK_ij, dV_ij)."""
+    B, H, Lq, D = Qi.shape
+    Lk = Kj.shape[2]
+    dQ = np.empty((B, H, Lq, D))
+    dK = np.empty((B, H, Lk, D))
+    dV = np.empty((B, H, Lk, Vj.shape[3]))
+    for b in range(B):
+        for h in range(H):
+            dQ[b, h], dK[b, h], dV[b, h] = backward_block(
+                Qi[b, h], Kj[b, h], Vj[b, h], dOi[b, h], lse_i[b, h], delta_i[b, h],
+                q_off, k_off, causal, scale)
+    return dQ, dK, dV
+
+
+def rank_backward(i: int, Q_i: np.ndarray, K_ranks: np.ndarray, V_ranks: np.ndarray,
+                  dO_i: np.ndarray, lse_i: np.ndarray, delta_i: np.ndarray, pos: np.ndarray,
+                  causal: bool, scale: float | None = None):
+    """Rank i's ring backward: dQ_i summed over every K/V block (in ring
+    order), and rank i's contributions to every block's dK, dV (in a
+    multi-GPU ring these accumulators travel with K/V and return to their
+    owner).  Returns (dQ_i [B, H, L/N, D], dK [N, ...], dV [N, ...])."""
+    N = pos.shape[0]
+    dQ = np.zeros_like(Q_i)
+    dK = np.zeros_like(K_ranks)
+    dV = np.zeros_like(V_ranks)
+    for j in ring_order(i, N):
+        dq, dk, dv = partial_backward(Q_i, K_ranks[j], V_ranks[j], dO_i, lse_i, delta_i,
+                                      pos[i], pos[j], causal, scale)
+        dQ += dq
+        dK[j] += dk
+        dV[j] += dv
+    return dQ, dK, dV
 
 
 # ---------------------------------------------------------------------------

@@ -333,11 +333,95 @@ def check_rope_global_positions(orc):
             assert not np.allclose(local[r], got[r])
 
 
+# -------------------------------------------------------------- backward pins
+
+def _sdpa_grads(Q, K, V, dO, causal):
+    """torch autograd through scaled_dot_product_attention, float64 on the CPU."""
+    q, k, v = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V))
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+    o.backward(torch.tensor(dO, dtype=torch.float64))
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def check_backward_autograd(orc):
+    """Gradients equal torch autograd of SDPA in float64 (causal and not)."""
+    for causal, (B, H, L, D), seed in [(True, (2, 2, 37, 16), 30), (False, (1, 3, 29, 8), 31),
+                                       (True, (1, 1, 70, 32), 32)]:
+        Q, K, V, dO = (_rand((B, H, L, D), seed + 100 * i) for i in range(4))
+        got = orc.attention_backward(Q, K, V, dO, causal)
+        want = _sdpa_grads(Q, K, V, dO, causal)
+        for g, w, name in zip(got, want, "QKV"):
+            assert np.max(np.abs(g - w)) < 1e-11, (causal, name, np.max(np.abs(g - w)))
+
+
+def check_backward_finite_differences(orc):
+    """Central differences of sum(dO * O) at every input entry (tiny case)."""
+    B, H, L, D = 1, 1, 5, 3
+    Q, K, V, dO = (_rand((B, H, L, D), 40 + i) for i in range(4))
+
+    def loss(Q_, K_, V_):
+        return float(np.sum(dO * orc.attention(Q_, K_, V_, True)[0]))
+
+    grads = orc.attention_backward(Q, K, V, dO, True)
+    h = 1e-6
+    for which, g in enumerate(grads):
+        for idx in np.ndindex(Q.shape):
+            args = [Q.copy(), K.copy(), V.copy()]
+            args[which][idx] += h
+            up = loss(*args)
+            args[which][idx] -= 2 * h
+            down = loss(*args)
+            assert abs((up - down) / (2 * h) - g[idx]) < 1e-7, (which, idx)
+
+
+def check_backward_ring_decomposition(orc):
+    """Block-by-block ring backward (final lse and delta per query row) over
+    a zigzag layout equals the whole-sequence gradients."""
+    B, H, L, D, N = 2, 2, 64, 8, 4
+    Q, K, V, dO = (_rand((B, H, L, D), 50 + i) for i in range(4))
+    dQ, dK, dV = orc.attention_backward(Q, K, V, dO, True)
+    O, lse = orc.attention(Q, K, V, True)
+    delta = orc.backward_delta(O, dO)
+    pos = orc.zigzag_layout(L, N)
+    Qr, Kr, Vr, dOr = (orc.permute_to_ranks(x, pos) for x in (Q, K, V, dO))
+    lser = np.stack([lse[:, :, pos[r]] for r in range(N)])
+    der = np.stack([delta[:, :, pos[r]] for r in range(N)])
+    dQr = np.zeros_like(Qr)
+    dKr = np.zeros_like(Kr)
+    dVr = np.zeros_like(Vr)
+    for i in range(N):
+        dq, dk, dv = orc.rank_backward(i, Qr[i], Kr, Vr, dOr[i], lser[i], der[i], pos, True)
+        dQr[i] = dq
+        dKr += dk
+        dVr += dv
+    for got, want in ((dQr, dQ), (dKr, dK), (dVr, dV)):
+        assert np.max(np.abs(orc.permute_from_ranks(got, pos, L) - want)) < 1e-12
+
+
+def check_backward_invariants(orc):
+    """Adding one vector to every key leaves each softmax row unchanged, so
+    dK sums to zero over the keys; softmax rows sum to one, so dV sums to the
+    sum of dO over the queries; constant V makes O independent of the scores,
+    so dQ = dK = 0."""
+    B, H, L, D = 1, 2, 48, 16
+    Q, K, V, dO = (_rand((B, H, L, D), 60 + i) for i in range(4))
+    for causal in (True, False):
+        dQ, dK, dV = orc.attention_backward(Q, K, V, dO, causal)
+        assert np.max(np.abs(dK.sum(axis=2))) < 1e-12
+        assert np.max(np.abs(dV.sum(axis=2) - dO.sum(axis=2))) < 1e-12
+        assert np.max(np.abs(dQ)) > 1e-3
+    Vc = np.broadcast_to(_rand((B, H, 1, D), 64), (B, H, L, D)).copy()
+    dQ, dK, dV = orc.attention_backward(Q, K, Vc, dO, True)
+    assert np.max(np.abs(dQ)) < 1e-12 and np.max(np.abs(dK)) < 1e-12
+
+
 PINS = [check_layout_golden, check_layout_permutation, check_layout_balance, check_ring_order,
         check_permute, check_brute_force, check_sdpa, check_uniform_scores,
         check_constant_v_and_first_row, check_chunk_merge_invariant, check_partial_empty_rows,
         check_merge_algebra, check_structural, check_sampled_rows, check_rope_sinusoid_table,
-        check_rope_norm_and_identity, check_rope_relative, check_rope_global_positions]
+        check_rope_norm_and_identity, check_rope_relative, check_rope_global_positions,
+        check_backward_autograd, check_backward_finite_differences,
+        check_backward_ring_decomposition, check_backward_invariants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -390,6 +474,18 @@ MUTANTS = {
     "rope half pairing": ("return k, k + D // 2", "return k, D - 1 - k"),
     "rope local positions": ("rope(x[:, :, pos[r]], pos[r], base, pairing)",
                              "rope(x[:, :, pos[r]], np.arange(pos.shape[1]), base, pairing)"),
+    "bwd transposed scores": ("s = scale * (q @ k.T)", "s = scale * (k @ q.T)"),
+    "bwd delta sign": ("dS = P * (dP - delta[:, None])", "dS = P * (dP + delta[:, None])"),
+    "bwd dropped delta": ("dS = P * (dP - delta[:, None])", "dS = P * dP"),
+    "bwd dv transposed": ("P.T @ dO", "P @ dO"),
+    "bwd dk scale": ("scale * (dS.T @ q)", "(dS.T @ q)"),
+    "bwd dq uses v": ("scale * (dS @ k)", "scale * (dS @ v)"),
+    "bwd lse": ("np.exp(s - np.where(fin, lse, 0.0)[:, None])[ok]", "np.exp(s)[ok]"),
+    "bwd delta definition": ("np.asarray(dO, dtype=np.float64) * np.asarray(O, dtype=np.float64)",
+                             "np.asarray(dO, dtype=np.float64) * np.asarray(dO, dtype=np.float64)"),
+    "bwd ring block": ("dK[j] += dk", "dK[i] += dk"),
+    "bwd causal key range": ("kend = (int(q_pos[a:b].max()) + 1) if causal",
+                             "kend = (int(q_pos[a:b].max())) if causal"),
     "rope position offset": ("phi = np.asarray(pos, dtype=np.float64)[:, None]",
                              "phi = (np.asarray(pos, dtype=np.float64)[:, None] + 1)"),
 }
