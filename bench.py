@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--ring", choices=("fused", "partials"), default="fused",
                     help="one fused launch per ring (default) or N partials + N-1 merges")
+    ap.add_argument("--backward", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the rank's ring backward (reported under kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -135,7 +137,7 @@ def main():
 
     import sequence_attention_cpa_amd as cpa
     from sequence_attention_cpa_amd.pipeline import SharePipeline
-    from sequence_attention_cpa_amd.workloads import WORKLOADS, make_inputs
+    from sequence_attention_cpa_amd.workloads import WORKLOADS, make_inputs, make_upstream_grad
 
     cpa.load()
     dev = "cuda:0"
@@ -210,6 +212,17 @@ def main():
     mevs = timed(lambda: cpa.merge(pipe.Or[0], pipe.lser[0], tO, tl), reps)
     pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr), reps)
     rope_evs = timed(lambda: cpa.zigzag_permute_rope(K, pos_d, w.N, 10000.0, out=pipe.Kr), reps)
+    # Ring backward of the same rank (delta + dQ pass + dK/dV pass), after a
+    # forward step so that O and lse are the ring's.
+    bwd_evs = []
+    if args.backward:
+        pipe.step(Q, K, V)
+        dO = make_upstream_grad(w).to(dev)
+        pipe.backward(dO)
+        bwd_evs = timed(lambda: cpa.rank_backward(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr, pos_d,
+                                                  pipe.Or[0], pipe.dOr[0], pipe.lser[0],
+                                                  w.causal, pipe.dKr, pipe.dVr, pipe.scale,
+                                                  dQ=pipe.dQr[0], delta=pipe.deltar[0]), reps)
     torch.cuda.synchronize()
     p_ms = np.array([a.elapsed_time(b) for _, (a, b) in part_evs])
     p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _ in part_evs])
@@ -229,6 +242,12 @@ def main():
     perm_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
     perm_bytes = 2 * K.numel() * K.element_size()
     rope_ms = float(np.mean([a.elapsed_time(b) for a, b in rope_evs]))
+    bwd = None
+    if bwd_evs:
+        b_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_evs]))
+        b_flop = 2.0 * useful  # dV, dP, dQ, dK: 4 products of 2*D per visible pair
+        bwd = {"ms": round(b_ms, 4), "TFLOP/s": round(b_flop / (b_ms * 1e-3) / 1e12, 2),
+               "useful_flop": b_flop}
 
     value = useful / (ms_step * 1e-3) / 1e12
     out = {
@@ -268,6 +287,7 @@ def main():
                                "GB/s": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
                                "bytes": perm_bytes},
             "ms_per_step_events": round(ms_step_ev, 4),
+            "rank_backward": bwd,
         },
         "cpu_baseline": None,
     }

@@ -163,6 +163,69 @@ cpa_status cpa_zigzag_permute(const void *src, void *dst, int32_t elem_bytes,
                               const int64_t *pos_all, int32_t N, int32_t rank_lo,
                               int32_t rank_hi, int32_t inverse, void *stream);
 
+/*
+ * Backward.  The pages give no backward; context parallelism serves training
+ * ("序列与上下文并行", 工程实践: CP is validated by comparing training losses),
+ * so the gradients of O = softmax(Q K^T * scale + mask) V are provided.  For
+ * an upstream gradient dO, with P = exp(scores - lse) on visible pairs:
+ *   delta_t = sum_d dO[t, d] O[t, d],   dS = P * (dO V^T - delta),
+ *   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+ * Under CP these hold block by block when lse and delta are the query rows'
+ * FINAL values (over every key they see), so a ring step needs only the
+ * rank's (Q, dO, lse, delta) and the block's (K, V).  Gradients are float32;
+ * bf16 inputs use the matrix cores with P and dS rounded to bf16.
+ */
+
+/*
+ * delta [rows] = sum over d of dO * O, the per-row term of the softmax
+ * derivative, computed once per rank before its ring steps.
+ *   O      device float32 [rows, D] (the forward's output)
+ *   dO     device [rows, D] of `dt`
+ *   delta  device float32 [rows] (written)
+ * D in {16, 64, 128}.
+ */
+cpa_status cpa_backward_delta(const float *O, const void *dO, cpa_dtype dt, int64_t rows,
+                              int32_t D, float *delta, void *stream);
+
+/*
+ * One ring step of the backward: the gradient contributions of Q_i against
+ * (K_j, V_j), ADDED into dQ, dK and dV (so steps accumulate).
+ *   Q, dO         device [B, H, Lq, D] of `dt`;  K, V device [B, H, Lk, D] of `dt`
+ *   lse, delta    device float32 [B, H, Lq]: the query rows' final values
+ *                 (a row with lse = -inf contributes nothing)
+ *   q_off, k_off, causal, scale   as for cpa_partial
+ *   dQ            device float32 [B, H, Lq, D] (read and written)
+ *   dK, dV        device float32 [B, H, Lk, D] (read and written)
+ * D in {16, 64, 128}; bf16 with D = 64 or 128 runs on the matrix cores.
+ */
+cpa_status cpa_partial_backward(const void *Q, const void *K, const void *V, const void *dO,
+                                const float *lse, const float *delta, cpa_dtype dt, int32_t B,
+                                int32_t H, int64_t Lq, int64_t Lk, int32_t D,
+                                const int64_t *q_off, const int64_t *k_off, int32_t causal,
+                                float scale, float *dQ, float *dK, float *dV, void *stream);
+
+/*
+ * Rank i's ring backward: delta_i from (O_i, dO_i), then every K/V block in
+ * the forward's fused order.  dQ_i is WRITTEN (all blocks summed); rank i's
+ * contributions to every block's gradient are ADDED into dK_all / dV_all
+ * (zero them before the first rank; after all N ranks they hold the full
+ * dK, dV in rank-major order).  bf16 with D = 64 or 128 takes two launches
+ * besides delta (one for dQ over the whole ring, one for every block's dK/dV).
+ *   i, N, Q_i, K_all, V_all, pos_all, dt, B, H, L, D, causal, scale
+ *                 as for cpa_rank_forward
+ *   O_i, lse_i    device float32 [B, H, L/N, D] / [B, H, L/N]: rank i's forward
+ *   dO_i          device [B, H, L/N, D] of `dt`
+ *   dQ_i          device float32 [B, H, L/N, D] (written)
+ *   dK_all, dV_all device float32 rank-major [N, B, H, L/N, D] (read and written)
+ *   delta_i       device float32 [B, H, L/N] (written; kept for reuse)
+ */
+cpa_status cpa_rank_backward(int32_t i, int32_t N, const void *Q_i, const void *K_all,
+                             const void *V_all, const int64_t *pos_all, const float *O_i,
+                             const void *dO_i, const float *lse_i, cpa_dtype dt, int32_t B,
+                             int32_t H, int64_t L, int32_t D, int32_t causal, float scale,
+                             float *dQ_i, float *dK_all, float *dV_all, float *delta_i,
+                             void *stream);
+
 /* Pairing of the elements a rotary embedding rotates together. */
 typedef enum {
   CPA_ROPE_INTERLEAVED = 0, /* pairs (2k, 2k+1), as the sinusoidal table interleaves sin/cos */

@@ -12,7 +12,8 @@ from ._lib import (CPA_BF16, CPA_F32, CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED,  # no
                    CpaError, check, last_error, load, version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
-           "rank_forward_fused", "zigzag_permute", "rope", "zigzag_permute_rope", "last_error",
+           "rank_forward_fused", "zigzag_permute", "rope", "zigzag_permute_rope",
+           "backward_delta", "partial_backward", "rank_backward", "last_error",
            "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
 
 
@@ -184,3 +185,48 @@ def zigzag_permute_rope(src, pos_all, N: int, base: float = 10000.0,
                                          _ptr(pos_all), N, rank_lo, rank_hi, float(base),
                                          int(pairing), _stream(src)))
     return out
+
+
+def backward_delta(O, dO, out=None):
+    """delta [..., rows] = sum_d dO * O (O float32, dO bf16 or float32)."""
+    torch = _torch()
+    D = O.shape[-1]
+    rows = O.numel() // D
+    if out is None:
+        out = torch.empty(O.shape[:-1], dtype=torch.float32, device=O.device)
+    _need_gpu(O, dO, out)
+    check(load().cpa_backward_delta(_ptr(O), _ptr(dO), _dtype_code(dO), rows, D, _ptr(out),
+                                    _stream(O)))
+    return out
+
+
+def partial_backward(Q, K, V, dO, lse, delta, q_off, k_off, causal: bool, dQ, dK, dV,
+                     scale: float = 0.0):
+    """Add the gradient contributions of Q [B,H,Lq,D] against K/V [B,H,Lk,D]
+    into the float32 accumulators dQ, dK, dV (one ring step of the backward)."""
+    B, H, Lq, D = Q.shape
+    Lk = K.shape[2]
+    _need_gpu(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV)
+    check(load().cpa_partial_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(lse), _ptr(delta),
+                                      _dtype_code(Q), B, H, Lq, Lk, D, _ptr(q_off), _ptr(k_off),
+                                      int(bool(causal)), float(scale), _ptr(dQ), _ptr(dK),
+                                      _ptr(dV), _stream(Q)))
+    return dQ, dK, dV
+
+
+def rank_backward(i: int, N: int, Q_i, K_all, V_all, pos_all, O_i, dO_i, lse_i, causal: bool,
+                  dK_all, dV_all, scale: float = 0.0, dQ=None, delta=None):
+    """Rank i's ring backward: returns dQ_i (written) and adds rank i's
+    contributions into the rank-major float32 accumulators dK_all, dV_all."""
+    torch = _torch()
+    B, H, Lr, D = Q_i.shape
+    if dQ is None:
+        dQ = torch.empty((B, H, Lr, D), dtype=torch.float32, device=Q_i.device)
+    if delta is None:
+        delta = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
+    _need_gpu(Q_i, K_all, V_all, pos_all, O_i, dO_i, lse_i, dK_all, dV_all, dQ, delta)
+    check(load().cpa_rank_backward(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
+                                   _ptr(O_i), _ptr(dO_i), _ptr(lse_i), _dtype_code(Q_i), B, H,
+                                   Lr * N, D, int(bool(causal)), float(scale), _ptr(dQ),
+                                   _ptr(dK_all), _ptr(dV_all), _ptr(delta), _stream(Q_i)))
+    return dQ

@@ -46,4 +46,26 @@ hipError_t launch_rope(const void* src, void* dst, bool bf16, int64_t BH, int64_
                        int64_t nr, int D, const int64_t* pos, bool gather, double base, bool half,
                        hipStream_t stream);
 
+// Backward: delta[r] = sum_d dO[r, d] O[r, d] for `rows` rows (D in {16, 64, 128}).
+hipError_t launch_bwd_delta(const float* O, const void* dO, bool bf16, int64_t rows, int D,
+                            float* delta, hipStream_t stream);
+
+// Backward on the matrix cores (bf16, D = 64 or 128): dQ of the queries over
+// nblk K/V blocks (block b at K + b*kv_stride, positions k_off + b*koff_stride,
+// visited first+1, ..., first), written or added (acc_dq), and every block's
+// dK / dV contributions added into dK / dV (same block layout, fp32).
+hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const void* dO,
+                           const float* lse, const float* delta, const int64_t* q_off,
+                           const int64_t* k_off, float* dQ, float* dK, float* dV, int BH,
+                           int64_t Lq, int64_t Lk, int64_t kv_stride, int64_t koff_stride,
+                           int nblk, int first, int D, bool causal, float scale, bool acc_dq,
+                           hipStream_t stream);
+
+// Backward of one block, one row per thread in fp32 (fp32 inputs; bf16 with D = 16).
+hipError_t launch_bwd_rowwise(const void* Q, const void* K, const void* V, const void* dO,
+                              bool bf16, const float* lse, const float* delta,
+                              const int64_t* q_off, const int64_t* k_off, float* dQ, float* dK,
+                              float* dV, int BH, int64_t Lq, int64_t Lk, int D, bool causal,
+                              float scale, bool acc_dq, hipStream_t stream);
+
 }  // namespace cpa

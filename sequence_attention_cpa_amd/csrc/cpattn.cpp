@@ -281,4 +281,87 @@ cpa_status cpa_zigzag_permute_rope(const void* src, void* dst, cpa_dtype dt, int
                   "permute+rope launch");
 }
 
+cpa_status cpa_backward_delta(const float* O, const void* dO, cpa_dtype dt, int64_t rows,
+                              int32_t D, float* delta, void* stream) {
+  if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
+  if (rows < 0) return fail(CPA_ESHAPE, "rows must be >= 0");
+  if (!supported_d(D)) return fail(CPA_EUNSUPPORTED, "head_dim %d not built (16, 64, 128)", D);
+  if (rows == 0) return ok();
+  if (!O || !dO || !delta) return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(O, 16) || !aligned(dO, 16) || !aligned(delta, 4))
+    return fail(CPA_EINVAL, "O and dO must be 16-byte aligned, delta 4-byte");
+  return from_hip(cpa::launch_bwd_delta(O, dO, dt == CPA_BF16, rows, D, delta,
+                                        (hipStream_t)stream),
+                  "backward delta launch");
+}
+
+cpa_status cpa_partial_backward(const void* Q, const void* K, const void* V, const void* dO,
+                                const float* lse, const float* delta, cpa_dtype dt, int32_t B,
+                                int32_t H, int64_t Lq, int64_t Lk, int32_t D,
+                                const int64_t* q_off, const int64_t* k_off, int32_t causal,
+                                float scale, float* dQ, float* dK, float* dV, void* stream) {
+  cpa_status st = check_partial(Q, K, V, dt, B, H, Lq, Lk, D, q_off, k_off, causal, dQ, lse);
+  if (st != CPA_OK) return st;
+  if (Lq == 0 || Lk == 0) return ok();  // no pair: every contribution is zero
+  if (!dO || !delta || !dK || !dV) return fail(CPA_EINVAL, "null dO/delta/dK/dV pointer");
+  if (!aligned(dO, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(delta, 4))
+    return fail(CPA_EINVAL, "dO, dK and dV must be 16-byte aligned, delta 4-byte");
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
+  const int BH = B * H;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dt == CPA_BF16 && (D == 64 || D == 128))
+    e = cpa::launch_bwd_mfma(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV, BH, Lq, Lk, 0, 0,
+                             1, 0, D, causal != 0, scale, true, s);
+  else
+    e = cpa::launch_bwd_rowwise(Q, K, V, dO, dt == CPA_BF16, lse, delta, q_off, k_off, dQ, dK, dV,
+                                BH, Lq, Lk, D, causal != 0, scale, true, s);
+  return from_hip(e, "partial backward launch");
+}
+
+cpa_status cpa_rank_backward(int32_t i, int32_t N, const void* Q_i, const void* K_all,
+                             const void* V_all, const int64_t* pos_all, const float* O_i,
+                             const void* dO_i, const float* lse_i, cpa_dtype dt, int32_t B,
+                             int32_t H, int64_t L, int32_t D, int32_t causal, float scale,
+                             float* dQ_i, float* dK_all, float* dV_all, float* delta_i,
+                             void* stream) {
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (i < 0 || i >= N) return fail(CPA_EINVAL, "rank index %d outside [0, %d)", i, N);
+  const int64_t Lr = L / N;
+  if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
+  st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, dQ_i,
+                     lse_i);
+  if (st != CPA_OK) return st;
+  if (!O_i || !dO_i || !dK_all || !dV_all || !delta_i)
+    return fail(CPA_EINVAL, "null O/dO/dK/dV/delta pointer");
+  if (!aligned(O_i, 16) || !aligned(dO_i, 16) || !aligned(dK_all, 16) || !aligned(dV_all, 16) ||
+      !aligned(delta_i, 4))
+    return fail(CPA_EINVAL, "O, dO, dK and dV must be 16-byte aligned, delta 4-byte");
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
+  const int BH = B * H;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = cpa::launch_bwd_delta(O_i, dO_i, dt == CPA_BF16, (int64_t)BH * Lr, D, delta_i, s);
+  if (e != hipSuccess) return from_hip(e, "backward delta launch");
+  const int64_t* q_off = pos_all + (int64_t)i * Lr;
+  const int64_t blk = (int64_t)BH * Lr * D;  // elements per rank block
+  const size_t eb = dt == CPA_BF16 ? 2 : 4;
+  if (dt == CPA_BF16 && (D == 64 || D == 128)) {
+    e = cpa::launch_bwd_mfma(Q_i, K_all, V_all, dO_i, lse_i, delta_i, q_off, pos_all, dQ_i,
+                             dK_all, dV_all, BH, Lr, Lr, blk, Lr, N, i, D, causal != 0, scale,
+                             false, s);
+    return from_hip(e, "ring backward launch");
+  }
+  for (int32_t step = 0; step < N; ++step) {
+    const int32_t j = (i + step) % N;
+    const char* Kj = (const char*)K_all + (size_t)j * blk * eb;
+    const char* Vj = (const char*)V_all + (size_t)j * blk * eb;
+    e = cpa::launch_bwd_rowwise(Q_i, Kj, Vj, dO_i, dt == CPA_BF16, lse_i, delta_i, q_off,
+                                pos_all + (int64_t)j * Lr, dQ_i, dK_all + j * blk,
+                                dV_all + j * blk, BH, Lr, Lr, D, causal != 0, scale, step > 0, s);
+    if (e != hipSuccess) return from_hip(e, "ring backward launch");
+  }
+  return ok();
+}
+
 }  // extern "C"

@@ -1,0 +1,96 @@
+// Shared device helpers of the matrix-core attention kernels (forward and
+// backward): the bf16 operand types, the geometry and XOR swizzle of a
+// 32-row LDS tile, the asynchronous global-to-LDS copy, and the wave-wide
+// search of a sorted position table.  Header-only; every function inlines.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace cpa {
+namespace tile {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int BN = 32;         // rows of one LDS tile (keys, or queries in the dK/dV pass)
+
+template <int D>
+struct Geo {
+  static constexpr int CHUNKS = D / 8;               // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one K or V tile
+  static constexpr int KK = D / 16;                  // MFMA k-steps over d
+  static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
+  static constexpr int RPI = 1024 / ROW_BYTES;       // tile rows per 1 KB copy instruction
+  static constexpr int IPW = TILE_BYTES / 1024 / 4;  // copy instructions per wave per tile
+  static_assert(IPW >= 1, "tile smaller than one copy instruction per wave");
+};
+
+// Physical 16-byte chunk holding logical chunk c of tile row r (an XOR, so
+// it is its own inverse).  Depends on r only through r % 16.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    return c ^ ((r >> 1) & 7);
+  }
+}
+
+// Number of entries <= x in the increasing array off[0, n); wave-cooperative
+// 64-way search (every lane returns the same value).
+__device__ inline int64_t count_le(const int64_t* __restrict__ off, int64_t n, int64_t x) {
+  const int lane = threadIdx.x & 63;
+  int64_t lo = 0, hi = n;
+  while (hi - lo > 64) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t idx = lo + lane * step;
+    const bool p = idx < hi && off[idx] <= x;
+    const int c = __popcll(__ballot(p));
+    if (c == 0) return lo;
+    const int64_t nlo = lo + (int64_t)(c - 1) * step + 1;
+    const int64_t probe_c = lo + (int64_t)c * step;
+    hi = probe_c < hi ? probe_c : hi;
+    lo = nlo;
+  }
+  const int64_t idx = lo + lane;
+  const bool p = idx < hi && off[idx] <= x;
+  return lo + __popcll(__ballot(p));
+}
+
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+// Inline asm: the instruction has no register result, and hiding it from the
+// compiler keeps it from making unrelated LDS reads wait for it; completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the tile.
+__device__ __forceinline__ void copy16_saddr(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void copy16_vaddr(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
+
+}  // namespace tile
+}  // namespace cpa

@@ -15,12 +15,19 @@ With `rope_base` set, Q and K are rotated at their global positions on the
 way into rank-major order (cpa_zigzag_permute_rope: the rotary embedding is
 folded into the permute, so it costs no extra pass over memory).
 
-All buffers are allocated once in the constructor; `step` allocates nothing.
+`backward(dO)` runs the ring backward of the ranks after a `step`: dO is
+permuted like Q, each rank's cpa_rank_backward writes its dQ and adds its
+contributions to every block's dK / dV (rank-major float32 accumulators,
+cleared first), and the gradients are scattered back to global order.  With
+RoPE the returned dQ, dK are gradients with respect to the rotated Q, K.
+
+All buffers are allocated once in the constructor (the backward's on first
+use); `step` and `backward` allocate nothing after that.
 """
 from __future__ import annotations
 
-from . import (CPA_ROPE_INTERLEAVED, rank_forward, rank_forward_fused, rank_forward_workspace,
-               zigzag_layout, zigzag_permute, zigzag_permute_rope)
+from . import (CPA_ROPE_INTERLEAVED, rank_backward, rank_forward, rank_forward_fused,
+               rank_forward_workspace, zigzag_layout, zigzag_permute, zigzag_permute_rope)
 
 
 class SharePipeline:
@@ -75,3 +82,32 @@ class SharePipeline:
             else:
                 rank_forward(i, self.N, self.Qr[k], self.Kr, self.Vr, self.pos, self.causal,
                              self.scale, out=self.Or[k], lse=self.lser[k], workspace=self.ws)
+
+    def backward(self, dO):
+        """dO: global [B, H, L, D] (Q's dtype).  Returns global float32 (dQ, dK,
+        dV); dQ rows of ranks outside [rank_lo, rank_hi) are left zero, and
+        dK, dV hold the contributions of the selected ranks only."""
+        import torch
+
+        N, lo, hi = self.N, self.rank_lo, self.rank_hi
+        if not hasattr(self, "dOr"):
+            f32 = dict(dtype=torch.float32, device=self.Kr.device)
+            self.dOr = torch.empty_like(self.Qr)
+            self.dQr = torch.empty(self.Qr.shape, **f32)
+            self.deltar = torch.empty(self.lser.shape, **f32)
+            self.dKr = torch.empty(self.Kr.shape, **f32)
+            self.dVr = torch.empty(self.Vr.shape, **f32)
+            self.dQ = torch.zeros((self.B, self.H, self.L, self.D), **f32)
+            self.dK = torch.empty_like(self.dQ)
+            self.dV = torch.empty_like(self.dQ)
+        zigzag_permute(dO, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.dOr)
+        self.dKr.zero_()
+        self.dVr.zero_()
+        for k, i in enumerate(range(lo, hi)):
+            rank_backward(i, N, self.Qr[k], self.Kr, self.Vr, self.pos, self.Or[k], self.dOr[k],
+                          self.lser[k], self.causal, self.dKr, self.dVr, self.scale,
+                          dQ=self.dQr[k], delta=self.deltar[k])
+        zigzag_permute(self.dQr, self.pos, N, inverse=True, rank_lo=lo, rank_hi=hi, out=self.dQ)
+        zigzag_permute(self.dKr, self.pos, N, inverse=True, out=self.dK)
+        zigzag_permute(self.dVr, self.pos, N, inverse=True, out=self.dV)
+        return self.dQ, self.dK, self.dV

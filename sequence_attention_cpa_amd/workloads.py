@@ -111,6 +111,18 @@ def make_inputs(w: Workload):
     return out[0], out[1], out[2], idx
 
 
+def make_upstream_grad(w: Workload, seed_offset: int = 1000):
+    """dO for a backward pass: standard normal [B, H, L, D] from its own
+    generator (seed + seed_offset), in the workload's dtype (bf16 by torch's
+    round to nearest even)."""
+    import torch
+
+    rng = np.random.default_rng(w.seed + seed_offset)
+    g = rng.standard_normal((w.B, w.H, w.L, w.D), dtype=np.float32)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return torch.from_numpy(g).to(tdt)
+
+
 def sample_rows(w: Workload, rank: int, pos_rank: np.ndarray, n_rows: int,
                 outliers: np.ndarray, seed: int = 0) -> np.ndarray:
     """Local row indices of `rank` to check at sizes where every row is too many.

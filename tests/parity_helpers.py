@@ -19,6 +19,34 @@ LSE_REL = 1e-3
 F32_RTOL, F32_ATOL = 1e-5, 1e-6
 
 
+# Backward, bf16 inputs: P and dS are rounded to bf16 (relative 2^-9) before
+# the matrix products, whose sums are fp32, so every gradient entry carries an
+# error of a small multiple of 2^-9 times the size of its terms.  Checked
+# against the largest entry of the reference gradient (entries near zero
+# carry the same absolute error as large ones): max |d| <= 2e-2 max|ref| and
+# ||d||_2 <= 1e-2 ||ref||_2.  fp32 inputs: |d| <= 1e-5 |ref| + 1e-5 max|ref|
+# (dS = P (dP - delta) cancels, so a purely relative bound is too tight).
+GRAD_BF16_MAX_REL = 2e-2
+GRAD_BF16_NORM_REL = 1e-2
+GRAD_F32_RTOL = 1e-5
+GRAD_F32_ATOL_REL = 1e-5
+
+
+def assert_grad_close(got, ref, bf16, what=""):
+    d = np.abs(got - ref)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if bf16:
+        mx = float(d.max()) / max(scale, 1e-30) if d.size else 0.0
+        nrm = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)) if d.size else 0.0
+        assert mx <= GRAD_BF16_MAX_REL, f"{what}: max |d| = {mx:.3e} of max|ref| > {GRAD_BF16_MAX_REL}"
+        assert nrm <= GRAD_BF16_NORM_REL, f"{what}: norm-wise {nrm:.3e} > {GRAD_BF16_NORM_REL}"
+        return mx, nrm
+    bound = GRAD_F32_RTOL * np.abs(ref) + GRAD_F32_ATOL_REL * scale
+    worst = float((d / np.maximum(bound, 1e-300)).max()) if d.size else 0.0
+    assert np.all(d <= bound), f"{what}: fp32 gradient off by {worst:.2f}x tolerance"
+    return worst, 0.0
+
+
 def host_threads():
     try:
         n = len(os.sched_getaffinity(0))
