@@ -280,3 +280,72 @@ def _perm_rope(lib, **kw):
 def test_permute_rope_rejects(lib, kw, status):
     assert _perm_rope(lib, **kw) == status
     assert cpa.last_error() != ""
+
+
+def test_backward_delta_rejects(lib):
+    f = lib.cpa_backward_delta
+    assert f(P, P, 7, 10, 128, P, None) == _lib.CPA_EDTYPE
+    assert f(P, P, _lib.CPA_BF16, -1, 128, P, None) == _lib.CPA_ESHAPE
+    assert f(P, P, _lib.CPA_BF16, 10, 32, P, None) == _lib.CPA_EUNSUPPORTED
+    assert f(None, P, _lib.CPA_BF16, 10, 128, P, None) == _lib.CPA_EINVAL
+    assert f(P, P + 8, _lib.CPA_BF16, 10, 128, P, None) == _lib.CPA_EINVAL
+    assert f(None, None, _lib.CPA_BF16, 0, 128, None, None) == _lib.CPA_OK
+
+
+def _pbwd(lib, **kw):
+    a = dict(Q=P, K=P, V=P, dO=P, lse=P, delta=P, dt=_lib.CPA_BF16, B=1, H=2, Lq=64, Lk=64, D=128,
+             q_off=P, k_off=P, causal=1, scale=0.0, dQ=P, dK=P, dV=P, stream=None)
+    a.update(kw)
+    return lib.cpa_partial_backward(a["Q"], a["K"], a["V"], a["dO"], a["lse"], a["delta"], a["dt"],
+                                    a["B"], a["H"], a["Lq"], a["Lk"], a["D"], a["q_off"],
+                                    a["k_off"], a["causal"], a["scale"], a["dQ"], a["dK"],
+                                    a["dV"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=4), _lib.CPA_EDTYPE),
+    (dict(D=48), _lib.CPA_EUNSUPPORTED),
+    (dict(Lq=-2), _lib.CPA_ESHAPE),
+    (dict(H=0), _lib.CPA_ESHAPE),
+    (dict(Q=None), _lib.CPA_EINVAL),
+    (dict(dO=None), _lib.CPA_EINVAL),
+    (dict(delta=None), _lib.CPA_EINVAL),
+    (dict(dK=None), _lib.CPA_EINVAL),
+    (dict(dV=P + 4), _lib.CPA_EINVAL),
+    (dict(dO=P + 2), _lib.CPA_EINVAL),
+    (dict(k_off=None), _lib.CPA_EINVAL),
+])
+def test_partial_backward_rejects(lib, kw, status):
+    assert _pbwd(lib, **kw) == status
+    assert cpa.last_error() != ""
+
+
+def test_partial_backward_without_pairs_is_a_no_op(lib):
+    assert _pbwd(lib, Lq=0) == _lib.CPA_OK
+    assert _pbwd(lib, Lk=0, dK=None, dV=None) == _lib.CPA_OK
+
+
+def _rbwd(lib, **kw):
+    a = dict(i=0, N=4, Q=P, K=P, V=P, pos=P, O=P, dO=P, lse=P, dt=_lib.CPA_BF16, B=1, H=2, L=256,
+             D=128, causal=1, scale=0.0, dQ=P, dK=P, dV=P, delta=P, stream=None)
+    a.update(kw)
+    return lib.cpa_rank_backward(a["i"], a["N"], a["Q"], a["K"], a["V"], a["pos"], a["O"], a["dO"],
+                                 a["lse"], a["dt"], a["B"], a["H"], a["L"], a["D"], a["causal"],
+                                 a["scale"], a["dQ"], a["dK"], a["dV"], a["delta"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(i=4), _lib.CPA_EINVAL),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(L=260), _lib.CPA_ESHAPE),
+    (dict(D=8), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=3), _lib.CPA_EDTYPE),
+    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(O=None), _lib.CPA_EINVAL),
+    (dict(delta=None), _lib.CPA_EINVAL),
+    (dict(dK=P + 4), _lib.CPA_EINVAL),
+    (dict(lse=None), _lib.CPA_EINVAL),
+])
+def test_rank_backward_rejects(lib, kw, status):
+    assert _rbwd(lib, **kw) == status
+    assert cpa.last_error() != ""
