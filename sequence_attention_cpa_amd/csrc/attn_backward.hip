@@ -56,11 +56,14 @@ using I1 = std::integral_constant<int, 1>;
 // swz<D>: the async copy of a tile, the row-major operand (lane = row l32,
 // 8 columns starting at kk*16 + hi*8) and the transposed operand (lane = column
 // d of block db, 8 consecutive rows of half `h`, as two 4-row reads).
-template <int D>
+template <int D, int NW>
 struct TileAddr {
   using G = Geo<D>;
-  int coff[G::IPW];
-  int crow[G::IPW];
+  static constexpr int NCOPY = G::TILE_BYTES / 1024;         // 1 KB copy instructions per tile
+  static constexpr int IPW = NCOPY >= NW ? NCOPY / NW : 1;  // per copying wave
+  static constexpr int CW = NCOPY / IPW;                    // waves that copy
+  int coff[IPW];
+  int crow[IPW];
   int roff[G::KK];
   int toff[G::DB][2];
   int wv;
@@ -68,8 +71,8 @@ struct TileAddr {
   __device__ __forceinline__ TileAddr(int wv_, int lane) : wv(wv_) {
     const int hi = lane >> 5, l32 = lane & 31;
 #pragma unroll
-    for (int i = 0; i < G::IPW; ++i) {
-      const int n = wv * G::IPW + i;
+    for (int i = 0; i < IPW; ++i) {
+      const int n = (wv % CW) * IPW + i;
       crow[i] = n * G::RPI + lane / G::CHUNKS;
       coff[i] = crow[i] * G::ROW_BYTES + swz<D>(crow[i], lane % G::CHUNKS) * 16;
     }
@@ -90,18 +93,19 @@ struct TileAddr {
   // end re-read the last row (callers mask them).
   __device__ __forceinline__ void copy(const __bf16* src, int64_t row0, int64_t nrows,
                                        lds_char* dst) const {
+    if (wv >= CW) return;  // uniform per wave
     if (row0 + BN <= nrows) {
       const __bf16* base = src + row0 * D;
 #pragma unroll
-      for (int i = 0; i < G::IPW; ++i)
-        copy16_saddr((uint32_t)coff[i], base, lds_addr(dst + (wv * G::IPW + i) * 1024));
+      for (int i = 0; i < IPW; ++i)
+        copy16_saddr((uint32_t)coff[i], base, lds_addr(dst + (wv * IPW + i) * 1024));
     } else {
 #pragma unroll
-      for (int i = 0; i < G::IPW; ++i) {
+      for (int i = 0; i < IPW; ++i) {
         int64_t u = row0 + crow[i];
         u = u < nrows ? u : nrows - 1;
         const char* g = (const char*)(src + u * D) + (coff[i] - crow[i] * G::ROW_BYTES);
-        copy16_vaddr(g, lds_addr(dst + (wv * G::IPW + i) * 1024));
+        copy16_vaddr(g, lds_addr(dst + (wv * IPW + i) * 1024));
       }
     }
   }
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
       df[kk] = *reinterpret_cast<const bf16x8*>(dr + kk * 16 + hi * 8);
     }
   }
-  const TileAddr<D> ta(wv, lane);
+  const TileAddr<D, 4> ta(wv, lane);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -278,8 +282,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
 
 // ------------------------------------------------------------- dK/dV pass
 
+// Eight waves per workgroup, two per SIMD, for 128 keys: waves w and w + 4
+// share key group w (32 keys) and split every tile's four products evenly.
+// Wave w (P role) forms S = Q K^T and P, hands P to its partner through LDS,
+// and accumulates dV^T += dO^T P; wave w + 4 (dS role) forms dP = dO V^T,
+// then dS = P (dP - delta) from the partner's P, and accumulates
+// dK^T += Q^T dS.  A barrier in the middle of each tile publishes P.  Each
+// wave keeps one 32 x D accumulator and one of K / V, so two waves fit per
+// SIMD, and no product is computed twice.
 template <int D>
-__global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ dK,
@@ -293,12 +305,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char o_lds_raw[2 * TB];
   __shared__ __attribute__((aligned(16))) float l2_lds[2][BN];
   __shared__ __attribute__((aligned(16))) float dl_lds[2][BN];
+  __shared__ __attribute__((aligned(16))) float4 p_lds[4][4][64];  // [key group][r/4][lane]
   lds_char* const Ql = (lds_char*)q_lds_raw;
   lds_char* const Ol = (lds_char*)o_lds_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0 .. 7
+  const int kg = wv & 3;                                     // key group
+  const bool dk_role = wv >= 4;                              // dS role
   const int hi = lane >> 5;
   const int l32 = lane & 31;
   const int bh = blockIdx.x % BH;
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(
   const int blk = rest / n_ktiles;
   const int64_t k_base = (int64_t)kt * BM;
   const int64_t last_key = (k_base + BM < Lk ? k_base + BM : Lk) - 1;
-  const int64_t krow = k_base + wv * 32 + l32;
+  const int64_t krow = k_base + kg * 32 + l32;
   const int64_t krow_c = krow < Lk ? krow : Lk - 1;
   const float c_log2 = scale * LOG2E;
 
@@ -338,27 +353,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(
   const int t0 = (int)(m_lo / BN);
   const int T = (int)((Lq + BN - 1) / BN);
 
-  // K and V rows of this wave as B operands (lane: 8 columns of its key).
-  bf16x8 kf[KK], vf[KK];
-  {
-    const __bf16* kr = Kb + krow_c * D;
-    const __bf16* vr = Vb + krow_c * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(kr + kk * 16 + hi * 8);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(vr + kk * 16 + hi * 8);
-    }
-  }
-  const TileAddr<D> ta(wv, lane);
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.f;
-      dv[db][r] = 0.f;
-    }
+  const TileAddr<D, 8> ta(wv, lane);
   const f32x16 zero16 = {};
 
   // lse reference and delta of query tile t into LDS buffer b (first wave).
@@ -370,85 +365,117 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkdv_kernel(
     }
   };
 
-  auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
-    constexpr int P = decltype(P_)::value;
-    if (t + 1 < T) {
-      ta.copy(Qbh, (int64_t)(t + 1) * BN, Lq, Ql + (P ^ 1) * TB);
-      ta.copy(Obh, (int64_t)(t + 1) * BN, Lq, Ol + (P ^ 1) * TB);
+  // The whole pass for one role; both roles run the same copies, staging
+  // and barriers, so the workgroup stays in step.
+  auto run = [&](auto DKR_) __attribute__((always_inline)) {
+    constexpr bool DKR = decltype(DKR_)::value;
+    // This lane's key row of K (P role) or V (dS role) as the B operand.
+    bf16x8 rf[KK];
+    {
+      const __bf16* src = (DKR ? Vb : Kb) + krow_c * D;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        rf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16 + hi * 8);
     }
-    const lds_char* Qt = Ql + P * TB;
-    const lds_char* Ot = Ol + P * TB;
-    f32x16 s = zero16, dp = zero16;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.rows(Qt, kk), kf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.rows(Ot, kk), vf[kk], dp, 0, 0, 0);
-    }
-    // this lane's 16 queries: rows acc_row(r, hi) of the tile
-    float l2[16], dl[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 a = *reinterpret_cast<const float4*>(&l2_lds[P][g * 8 + hi * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&dl_lds[P][g * 8 + hi * 4]);
-      l2[g * 4 + 0] = a.x; l2[g * 4 + 1] = a.y; l2[g * 4 + 2] = a.z; l2[g * 4 + 3] = a.w;
-      dl[g * 4 + 0] = b.x; dl[g * 4 + 1] = b.y; dl[g * 4 + 2] = b.z; dl[g * 4 + 3] = b.w;
-    }
-    const int64_t q0 = (int64_t)t * BN;
-    if (q0 < m_hi) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (q0 + acc_row(r, hi) < my_first) s[r] = -INFINITY;
-    }
-    bf16x8 pf[2], dsf[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l2[r]));
-      pf[r >> 3][r & 7] = (__bf16)p;
-      dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[r]));
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.trans(Ot, h, db), pf[h], dv[db], 0, 0,
-                                                         0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.trans(Qt, h, db), dsf[h], dk[db], 0,
-                                                         0, 0);
-      }
-    if (t + 1 < T) stage_rows(t + 1, P ^ 1);
-    wait_copies();
-    __syncthreads();
-  };
-
-  ta.copy(Qbh, (int64_t)t0 * BN, Lq, Ql);
-  ta.copy(Obh, (int64_t)t0 * BN, Lq, Ol);
-  stage_rows(t0, 0);
-  wait_copies();
-  __syncthreads();
-  int t = t0;
-  for (; t + 1 < T; t += 2) {
-    iter(t, I0{});
-    iter(t + 1, I1{});
-  }
-  if (t < T) iter(t, I0{});
-
-  if (krow < Lk) {
-    float* krow_dk = dK + blk * kv_stride + ((int64_t)bh * Lk + krow) * D;
-    float* krow_dv = dV + blk * kv_stride + ((int64_t)bh * Lk + krow) * D;
+    f32x16 acc[DB];  // dV^T (P role) or dK^T (dS role), D x 32 keys
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = db * 32 + gq * 8 + hi * 4;
-        float4* pk = reinterpret_cast<float4*>(krow_dk + d);
-        float4* pv = reinterpret_cast<float4*>(krow_dv + d);
-        const float4 ok = *pk, ov = *pv;
-        *pk = float4{ok.x + dk[db][gq * 4 + 0] * scale, ok.y + dk[db][gq * 4 + 1] * scale,
-                     ok.z + dk[db][gq * 4 + 2] * scale, ok.w + dk[db][gq * 4 + 3] * scale};
-        *pv = float4{ov.x + dv[db][gq * 4 + 0], ov.y + dv[db][gq * 4 + 1],
-                     ov.z + dv[db][gq * 4 + 2], ov.w + dv[db][gq * 4 + 3]};
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float4* const pslot = &p_lds[kg][0][lane];
+
+    auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
+      constexpr int P = decltype(P_)::value;
+      if (t + 1 < T) {
+        ta.copy(Qbh, (int64_t)(t + 1) * BN, Lq, Ql + (P ^ 1) * TB);
+        ta.copy(Obh, (int64_t)(t + 1) * BN, Lq, Ol + (P ^ 1) * TB);
       }
-  }
+      const lds_char* Qt = Ql + P * TB;
+      const lds_char* Ot = Ol + P * TB;
+      const int64_t q0 = (int64_t)t * BN;
+      // S = Q K^T (P role) or dP = dO V^T (dS role): lane holds its key's
+      // 16 queries, rows acc_row(r, hi) = g*8 + hi*4 + (r & 3), r = 4g .. 4g+3.
+      f32x16 x = zero16;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.rows(DKR ? Ot : Qt, kk), rf[kk], x, 0, 0,
+                                                    0);
+      bf16x8 wf[2];
+      if constexpr (!DKR) {
+        if (q0 < m_hi) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (q0 + acc_row(r, hi) < my_first) x[r] = -INFINITY;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 a = *reinterpret_cast<const float4*>(&l2_lds[P][g * 8 + hi * 4]);
+          const float l2[4] = {a.x, a.y, a.z, a.w};
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(fmaf(x[g * 4 + e], c_log2, -l2[e]));
+            wf[(g * 4 + e) >> 3][(g * 4 + e) & 7] = (__bf16)pv[e];
+          }
+          pslot[g * 64] = float4{pv[0], pv[1], pv[2], pv[3]};
+        }
+      }
+      __syncthreads();  // P of this tile is in LDS
+      if constexpr (DKR) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 pv = pslot[g * 64];
+          const float4 b = *reinterpret_cast<const float4*>(&dl_lds[P][g * 8 + hi * 4]);
+          const float p4[4] = {pv.x, pv.y, pv.z, pv.w};
+          const float d4[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = g * 4 + e;
+            wf[r >> 3][r & 7] = (__bf16)(p4[e] * (x[r] - d4[e]));
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.trans(DKR ? Qt : Ot, h, db), wf[h],
+                                                            acc[db], 0, 0, 0);
+      if (t + 1 < T) stage_rows(t + 1, P ^ 1);
+      wait_copies();
+      __syncthreads();
+    };
+
+    ta.copy(Qbh, (int64_t)t0 * BN, Lq, Ql);
+    ta.copy(Obh, (int64_t)t0 * BN, Lq, Ol);
+    stage_rows(t0, 0);
+    wait_copies();
+    __syncthreads();
+    int t = t0;
+    for (; t + 1 < T; t += 2) {
+      iter(t, I0{});
+      iter(t + 1, I1{});
+    }
+    if (t < T) iter(t, I0{});
+
+    if (krow < Lk) {
+      float* dst = (DKR ? dK : dV) + blk * kv_stride + ((int64_t)bh * Lk + krow) * D;
+      const float f = DKR ? scale : 1.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float4* p = reinterpret_cast<float4*>(dst + db * 32 + gq * 8 + hi * 4);
+          const float4 o = *p;
+          *p = float4{o.x + acc[db][gq * 4 + 0] * f, o.y + acc[db][gq * 4 + 1] * f,
+                      o.z + acc[db][gq * 4 + 2] * f, o.w + acc[db][gq * 4 + 3] * f};
+        }
+    }
+  };
+  if (dk_role)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ------------------------------------------------------------- delta
@@ -671,7 +698,7 @@ hipError_t mfma_bwd(const void* Q, const void* K, const void* V, const void* dO,
                      causal ? 1 : 0, scale, n_qtiles, acc_dq ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(nblk * n_ktiles * BH)), dim3(NTHREADS),
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(nblk * n_ktiles * BH)), dim3(2 * NTHREADS),
                      0, st, (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V,
                      (const __bf16*)dO, lse, delta, q_off, k_off, dK, dV, BH, Lq, Lk, kv_stride,
                      koff_stride, causal ? 1 : 0, scale, n_ktiles);
