@@ -168,16 +168,17 @@ def main():
     for _ in range(args.warmup):
         pipe.step(Q, K, V)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs_step = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs_step[0].record(stream)
+    for k in range(args.steps):
         pipe.step(Q, K, V)
-    ev1.record(stream)
+        evs_step[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    ms_step_ev = ev0.elapsed_time(ev1) / args.steps
+    step_ms = np.array([evs_step[k].elapsed_time(evs_step[k + 1]) for k in range(args.steps)])
+    ms_step_ev = float(step_ms.mean())
 
     # Per-kernel timing on the same stream: the fused ring launch, the ring's
     # partials (same kernel and arguments as inside cpa_rank_forward), its
@@ -198,10 +199,15 @@ def main():
             evs.append((a, b))
         return evs
 
-    fused_evs = []
+    fused_evs, last_evs = [], []
     if w.dtype == "bf16" and w.D in (64, 128):
         fused_evs = timed(lambda: cpa.rank_forward_fused(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr,
                                                          pos_d, w.causal, out=tO, lse=tl), reps)
+        # Balance: the last rank's ring does the same causal work under zigzag.
+        other = w.N - 1 if rank != w.N - 1 else 0
+        Q_other = cpa.zigzag_permute(Q, pos_d, w.N, rank_lo=other, rank_hi=other + 1)[0]
+        last_evs = timed(lambda: cpa.rank_forward_fused(other, w.N, Q_other, pipe.Kr, pipe.Vr,
+                                                        pos_d, w.causal, out=tO, lse=tl), reps)
     part_evs = []
     for _ in range(reps):
         for s in range(w.N):
@@ -228,6 +234,11 @@ def main():
     p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _ in part_evs])
     p_avg_ms = float(p_ms.mean())
     f_ms = np.array([a.elapsed_time(b) for a, b in fused_evs]) if fused_evs else None
+    o_ms = np.array([a.elapsed_time(b) for a, b in last_evs]) if last_evs else None
+
+    def stats(x):
+        return {"median": round(float(np.median(x)), 4), "min": round(float(np.min(x)), 4),
+                "p90": round(float(np.percentile(x, 90)), 4)}
     if fused:
         dom_kernel = f"partial_attn_mfma_kernel<{w.D}> (one launch, {w.N} K/V blocks)"
         dom_ms = float(f_ms.mean())
@@ -276,6 +287,9 @@ def main():
         "kernels": {
             "ring": args.ring,
             "fused_ring_ms": round(float(f_ms.mean()), 4) if f_ms is not None else None,
+            "fused_ring_ms_stats": stats(f_ms) if f_ms is not None else None,
+            "fused_ring_ms_other_rank": ({"rank": other, **stats(o_ms)}
+                                         if o_ms is not None else None),
             "partial_ms": [round(float(x), 4) for x in p_ms[: w.N]],
             "partial_TFLOP/s": round(float(p_flops.mean()) / (p_avg_ms * 1e-3) / 1e12, 2),
             "merge": {"ms": round(m_ms, 4), "GB/s": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
@@ -287,6 +301,7 @@ def main():
                                "GB/s": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
                                "bytes": perm_bytes},
             "ms_per_step_events": round(ms_step_ev, 4),
+            "step_ms_stats": stats(step_ms),
             "rank_backward": bwd,
         },
         "cpu_baseline": None,

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   // n_hi bound it for the whole tile, my_n is this row's.
   const __bf16* Kbh = nullptr;
   const __bf16* Vbh = nullptr;
-  int64_t n_lo = Lk, n_hi = Lk, my_n = Lk;
+  // Indices into a block fit 32 bits (the host caps Lk at 2^30).
+  int n_lo = (int)Lk, n_hi = (int)Lk, my_n = (int)Lk;
   int T = 0;
 
   // ---- per-lane constants -------------------------------------------------
@@ -190,13 +191,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   auto finish_scores = [&](int j, f32x16 (&sj)[NKB], bf16x8 (&pprev)[NKB][2], auto HAS_PREV_)
                            __attribute__((always_inline)) {
     constexpr bool HAS_PREV = decltype(HAS_PREV_)::value;
-    const int64_t u0 = (int64_t)j * BN;
+    const int u0 = j * BN;
     if (u0 + BN > n_lo) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t u = u0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          const int u = u0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
           if (u >= my_n) sj[kb][r] = -INFINITY;
         }
     }
@@ -311,17 +312,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
   if (causal) {
     const int64_t* kb_off = k_off + blk * koff_stride;
-    n_lo = count_le(kb_off, Lk, q_first);
-    n_hi = count_le(kb_off, Lk, q_last);
-    int64_t lo = n_lo, hb = n_hi;  // first u in [n_lo, n_hi) with position > my_qpos
+    n_lo = (int)count_le(kb_off, Lk, q_first);
+    n_hi = (int)count_le(kb_off, Lk, q_last);
+    int lo = n_lo, hb = n_hi;  // first u in [n_lo, n_hi) with position > my_qpos
     while (lo < hb) {
-      const int64_t mid = (lo + hb) >> 1;
+      const int mid = (lo + hb) >> 1;
       if (kb_off[mid] <= my_qpos) lo = mid + 1; else hb = mid;
     }
     my_n = lo;
   }
   if (n_hi == 0) continue;  // no row of this tile sees any key of this block
-  T = (int)((n_hi + BN - 1) / BN);
+  T = (n_hi + BN - 1) / BN;
 
   // Prologue: K(0), K(1) into LDS; scores of tile 0.
   copy_tile(Kbh, 0, Kl);
@@ -343,16 +344,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     iter(0, I0{}, BF{}, BF{});
   } else {
     iter(0, I0{}, BF{}, BT{});
-    int t = 1;
+    int t = 1;  // odd on every entry to the loop body and after it
     for (; t + 2 < T; t += 2) {
       iter(t, I1{}, BT{}, BT{});
       iter(t + 1, I0{}, BT{}, BT{});
     }
-    if (t == T - 2) {
-      if (t & 1) iter(t, I1{}, BT{}, BT{}); else iter(t, I0{}, BT{}, BT{});
-      ++t;
+    if (t == T - 2) {  // T even: one more full iteration (odd t), then the last (even)
+      iter(t, I1{}, BT{}, BT{});
+      iter(t + 1, I0{}, BT{}, BF{});
+    } else {           // T odd: t = T - 1 is the last
+      iter(t, I1{}, BT{}, BF{});
     }
-    if (t & 1) iter(t, I1{}, BT{}, BF{}); else iter(t, I0{}, BT{}, BF{});
   }
 
   // Epilogue: PV(T-1).
