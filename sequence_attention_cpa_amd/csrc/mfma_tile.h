@@ -78,9 +78,15 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // Inline asm: the instruction has no register result, and hiding it from the
 // compiler keeps it from making unrelated LDS reads wait for it; completion is
 // awaited explicitly (vmcnt) before the barrier that publishes the tile.
+// `sbase` must be uniform across the wave; it is read from the first lane so
+// that it always lands in SGPRs, whatever the compiler inferred.
 __device__ __forceinline__ void copy16_saddr(uint32_t voff, const void* sbase, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const void* sb = (const void*)(uintptr_t)((hi << 32) | lo);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 __device__ __forceinline__ void copy16_vaddr(const void* gptr, uint32_t lds) {

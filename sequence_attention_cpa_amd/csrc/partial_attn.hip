@@ -22,7 +22,7 @@
 //  * Software pipeline: iteration t issues the matrix work of PV(t-1) and
 //    QK^T(t+1) together with the exponentials of tile t in one straight-line
 //    block, so the wave's own VALU work can issue in the shadow of its MFMAs
-//    (operands are fetched three MFMAs ahead).  Only the row max of tile t+1
+//    (operands are fetched four MFMAs ahead).  Only the row max of tile t+1
 //    and the rare rescale run between the matrix phases.  (Pinning the
 //    interleave with sched_group_barrier measured slower than the compiler's
 //    own schedule.)
@@ -180,8 +180,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   f32x16 s[2][NKB];        // scores of two tiles (S^T layout), by tile parity
   bf16x8 pf[2][NKB][2];    // bf16 P of two tiles, by tile parity
   float m2 = -INFINITY;  // exponent reference: an integer (log2 units) or -inf
-  float lsum = 0.f;      // this lane's share of the row sum of bf16 P (normalises O)
-  float lsum_f = 0.f;    // the same sum in fp32, before rounding (gives lse)
+  // This lane's share of the row sum of the bf16 P (normalises O) and of the
+  // same sum in fp32 (gives lse), kept as 2 and 4 independent partial sums so
+  // that the adds of one tile do not form one long dependent chain.
+  float lsum2[2] = {0.f, 0.f};
+  float lsum_f4[4] = {0.f, 0.f, 0.f, 0.f};
   const f32x16 zero16 = {};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -214,8 +217,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_amdgcn_ldexpf(acc[db][r], k);
-      lsum = __builtin_amdgcn_ldexpf(lsum, k);
-      lsum_f = __builtin_amdgcn_ldexpf(lsum_f, k);
+      lsum2[0] = __builtin_amdgcn_ldexpf(lsum2[0], k);
+      lsum2[1] = __builtin_amdgcn_ldexpf(lsum2[1], k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum_f4[i] = __builtin_amdgcn_ldexpf(lsum_f4[i], k);
       if constexpr (HAS_PREV) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     constexpr int NV = HAS_PV ? 2 * NKB * DB : 0;
     constexpr int NQ = HAS_QK ? NKB * KK : 0;
     constexpr int NM = NV + NQ;
-    constexpr int PF = 3;  // operands in flight ahead of the MFMA using them
+    constexpr int PF = 4;  // operands in flight ahead of the MFMA using them
     auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
       if (i < NV) {
         const int kb = i / (2 * DB), half = (i / DB) & 1, db = i % DB;
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[P][kb][r], c_log2, -m_use));
-        lsum_f += p;
+        lsum_f4[r & 3] += p;
         pf[P][kb][r >> 3][r & 7] = (__bf16)p;
       }
 #pragma unroll
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pair = {pf[P][kb][h][e], pf[P][kb][h][e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
+          lsum2[h] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum2[h], false);
         }
     if constexpr (HAS_QK) finish_scores(t + 1, s[P ^ 1], pf[P], std::true_type{});
     wait_copies();
@@ -381,8 +386,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   __syncthreads();  // the next block refills both LDS buffers
   }  // blocks
 
-  const float ltot = xhalf_sum(lsum);
-  const float ltot_f = xhalf_sum(lsum_f);
+  const float ltot = xhalf_sum(lsum2[0] + lsum2[1]);
+  const float ltot_f = xhalf_sum((lsum_f4[0] + lsum_f4[1]) + (lsum_f4[2] + lsum_f4[3]));
   if (qrow < Lq) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     float* orow = Obh + qrow * D;
