@@ -125,6 +125,32 @@ struct TileAddr {
   }
 };
 
+// Consume registers loaded from global memory before a loop: the compiler then
+// waits for those loads once, here, instead of treating them as possibly
+// pending inside the loop, where its waits would also cover the asynchronous
+// tile copies in flight (the hardware counts both in vmcnt).
+__device__ __forceinline__ void settle(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+
+// Two phases of matrix products whose A operands come from LDS: NM1 products,
+// then `between()` (the VALU work that produces the second phase's B
+// operands), then NM2 products.  Operands are fetched PF products ahead
+// (fetch(i) for product i), also across `between()`, so LDS latency hides
+// behind the matrix work instead of stalling every product.
+template <int NM1, int NM2, int PF, typename Fetch, typename Mma, typename Between>
+__device__ __forceinline__ void mfma_phases(Fetch&& fetch, Mma&& mma, Between&& between) {
+  constexpr int NM = NM1 + NM2;
+  bf16x8 ob[PF];
+#pragma unroll
+  for (int i = 0; i < PF && i < NM; ++i) ob[i] = fetch(i);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i == NM1) between();
+    const bf16x8 cur = ob[i % PF];
+    if (i + PF < NM) ob[i % PF] = fetch(i + PF);
+    mma(i, cur);
+  }
+}
+
 // Row offset (within a 32-row tile) of accumulator element r of a lane in
 // half-wave hi, for v_mfma_f32_32x32x16 (rows of the 32x32 result).
 __device__ __forceinline__ int acc_row(int r, int hi) { return (r >> 2) * 8 + hi * 4 + (r & 3); }
@@ -182,6 +208,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
       qf[kk] = *reinterpret_cast<const bf16x8*>(qr + kk * 16 + hi * 8);
       df[kk] = *reinterpret_cast<const bf16x8*>(dr + kk * 16 + hi * 8);
     }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      settle(qf[kk]);
+      settle(df[kk]);
+    }
   }
   const TileAddr<D, 4> ta(wv, lane);
 
@@ -206,29 +237,39 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     const lds_char* Kt = Kl + P * TB;
     const lds_char* Vt = Vl + P * TB;
     f32x16 s = zero16, dp = zero16;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.rows(Kt, kk), qf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.rows(Vt, kk), df[kk], dp, 0, 0, 0);
-    }
-    const int64_t u0 = (int64_t)t * BN;
-    if (u0 + BN > n_lo) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (u0 + acc_row(r, hi) >= my_n) s[r] = -INFINITY;
-    }
     bf16x8 dsf[2];
+    const int64_t u0 = (int64_t)t * BN;
+    // S^T, dP^T (K and V rows alternate), then dS, then dQ^T += K^T dS^T.
+    mfma_phases<2 * KK, 2 * DB, 3>(
+        [&](int i) __attribute__((always_inline)) -> bf16x8 {
+          if (i < 2 * KK) return ta.rows((i & 1) ? Vt : Kt, i >> 1);
+          const int j = i - 2 * KK;
+          return ta.trans(Kt, j / DB, j % DB);
+        },
+        [&](int i, const bf16x8& op) __attribute__((always_inline)) {
+          if (i < 2 * KK) {
+            if (i & 1)
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, df[i >> 1], dp, 0, 0, 0);
+            else
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[i >> 1], s, 0, 0, 0);
+          } else {
+            const int j = i - 2 * KK;
+            acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, dsf[j / DB], acc[j % DB], 0,
+                                                                  0, 0);
+          }
+        },
+        [&]() __attribute__((always_inline)) {
+          if (u0 + BN > n_lo) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l2));
-      dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
-    }
+            for (int r = 0; r < 16; ++r)
+              if (u0 + acc_row(r, hi) >= my_n) s[r] = -INFINITY;
+          }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.trans(Kt, h, db), dsf[h], acc[db],
-                                                          0, 0, 0);
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l2));
+            dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
+          }
+        });
     wait_copies();
     __syncthreads();
   };
@@ -376,6 +417,8 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         rf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16 + hi * 8);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) settle(rf[kk]);
     }
     f32x16 acc[DB];  // dV^T (P role) or dK^T (dS role), D x 32 keys
 #pragma unroll
@@ -395,52 +438,61 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
       const int64_t q0 = (int64_t)t * BN;
       // S = Q K^T (P role) or dP = dO V^T (dS role): lane holds its key's
       // 16 queries, rows acc_row(r, hi) = g*8 + hi*4 + (r & 3), r = 4g .. 4g+3.
+      // Then P (published through LDS) or dS, then dV^T += dO^T P or
+      // dK^T += Q^T dS.
       f32x16 x = zero16;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.rows(DKR ? Ot : Qt, kk), rf[kk], x, 0, 0,
-                                                    0);
       bf16x8 wf[2];
-      if constexpr (!DKR) {
-        if (q0 < m_hi) {
+      mfma_phases<KK, 2 * DB, 3>(
+          [&](int i) __attribute__((always_inline)) -> bf16x8 {
+            if (i < KK) return ta.rows(DKR ? Ot : Qt, i);
+            const int j = i - KK;
+            return ta.trans(DKR ? Qt : Ot, j / DB, j % DB);
+          },
+          [&](int i, const bf16x8& op) __attribute__((always_inline)) {
+            if (i < KK) {
+              x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, rf[i], x, 0, 0, 0);
+            } else {
+              const int j = i - KK;
+              acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, wf[j / DB], acc[j % DB],
+                                                                    0, 0, 0);
+            }
+          },
+          [&]() __attribute__((always_inline)) {
+            if constexpr (!DKR) {
+              if (q0 < m_hi) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (q0 + acc_row(r, hi) < my_first) x[r] = -INFINITY;
-        }
+                for (int r = 0; r < 16; ++r)
+                  if (q0 + acc_row(r, hi) < my_first) x[r] = -INFINITY;
+              }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 a = *reinterpret_cast<const float4*>(&l2_lds[P][g * 8 + hi * 4]);
-          const float l2[4] = {a.x, a.y, a.z, a.w};
-          float pv[4];
+              for (int g = 0; g < 4; ++g) {
+                const float4 a = *reinterpret_cast<const float4*>(&l2_lds[P][g * 8 + hi * 4]);
+                const float l2[4] = {a.x, a.y, a.z, a.w};
+                float pv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pv[e] = __builtin_amdgcn_exp2f(fmaf(x[g * 4 + e], c_log2, -l2[e]));
-            wf[(g * 4 + e) >> 3][(g * 4 + e) & 7] = (__bf16)pv[e];
-          }
-          pslot[g * 64] = float4{pv[0], pv[1], pv[2], pv[3]};
-        }
-      }
-      __syncthreads();  // P of this tile is in LDS
-      if constexpr (DKR) {
+                for (int e = 0; e < 4; ++e) {
+                  pv[e] = __builtin_amdgcn_exp2f(fmaf(x[g * 4 + e], c_log2, -l2[e]));
+                  wf[(g * 4 + e) >> 3][(g * 4 + e) & 7] = (__bf16)pv[e];
+                }
+                pslot[g * 64] = float4{pv[0], pv[1], pv[2], pv[3]};
+              }
+            }
+            __syncthreads();  // P of this tile is in LDS
+            if constexpr (DKR) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 pv = pslot[g * 64];
-          const float4 b = *reinterpret_cast<const float4*>(&dl_lds[P][g * 8 + hi * 4]);
-          const float p4[4] = {pv.x, pv.y, pv.z, pv.w};
-          const float d4[4] = {b.x, b.y, b.z, b.w};
+              for (int g = 0; g < 4; ++g) {
+                const float4 pv = pslot[g * 64];
+                const float4 b = *reinterpret_cast<const float4*>(&dl_lds[P][g * 8 + hi * 4]);
+                const float p4[4] = {pv.x, pv.y, pv.z, pv.w};
+                const float d4[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = g * 4 + e;
-            wf[r >> 3][r & 7] = (__bf16)(p4[e] * (x[r] - d4[e]));
-          }
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.trans(DKR ? Qt : Ot, h, db), wf[h],
-                                                            acc[db], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) {
+                  const int r = g * 4 + e;
+                  wf[r >> 3][r & 7] = (__bf16)(p4[e] * (x[r] - d4[e]));
+                }
+              }
+            }
+          });
       if (t + 1 < T) stage_rows(t + 1, P ^ 1);
       wait_copies();
       __syncthreads();
