@@ -122,6 +122,8 @@ RANK_BWD_CASES = [
     (torch.bfloat16, 1, 2, 1536, 4, 128, False, True),
     (torch.bfloat16, 1, 2, 2048, 1, 128, True, True),
     (torch.bfloat16, 1, 2, 256, 16, 128, True, True),   # chunks of 8: every tile masked
+    (torch.bfloat16, 1, 2, 1000, 4, 128, True, True),   # 250 rows per rank: ragged tiles
+    (torch.bfloat16, 2, 3, 1000, 4, 64, True, True),
     (torch.float32, 1, 2, 64, 4, 16, True, False),      # the fp32 tiny shape
     (torch.bfloat16, 1, 2, 128, 4, 16, True, False),    # bf16 D=16 (row kernels)
 ]
@@ -216,3 +218,23 @@ def test_ring_backward_128k_sampled():
     sum_dO = dO.double().sum(dim=2).numpy()
     assert np.all(np.abs(sum_dK) <= 1e-3 * abs_dK), float(np.max(np.abs(sum_dK) / abs_dK))
     assert np.all(np.abs(sum_dV - sum_dO) <= 1e-3 * dO.double().abs().sum(dim=2).numpy())
+
+
+def test_partial_backward_explicit_scale():
+    """A caller-given scale reaches P, dQ and dK (not only the default 1/sqrt(D))."""
+    B, H, L, D, scale = 1, 2, 160, 128, 0.05
+    Q, K, V, dO = (rand((B, H, L, D), torch.bfloat16, 120 + i) for i in range(4))
+    off = np.arange(L, dtype=np.int64)
+    Q64, K64, V64, dO64 = (widen(x) for x in (Q, K, V, dO))
+    O, lse = cpa_oracle.partial(Q64, K64, V64, off, off, True, scale)
+    delta = cpa_oracle.backward_delta(O, dO64)
+    ref = cpa_oracle.partial_backward(Q64, K64, V64, dO64, lse, delta, off, off, True, scale)
+    acc = [torch.zeros(x.shape, device=DEV) for x in (Q, K, V)]
+    offd = torch.from_numpy(off).to(DEV)
+    cpa.partial_backward(Q.to(DEV), K.to(DEV), V.to(DEV), dO.to(DEV),
+                         torch.from_numpy(lse).float().to(DEV),
+                         torch.from_numpy(delta).float().to(DEV), offd, offd, True, *acc,
+                         scale=scale)
+    torch.cuda.synchronize()
+    for name, a, r in zip(("dQ", "dK", "dV"), acc, ref):
+        assert_grad_close(a.cpu().double().numpy(), r, True, f"scale {name}")

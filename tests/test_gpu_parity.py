@@ -349,6 +349,8 @@ FUSED_CASES = [
     (2, 2, 1024, 4, 64, True),
     (1, 2, 1536, 4, 128, False),
     (1, 2, 256, 16, 128, True),   # chunks of 8 keys: every tile of every block is masked
+    (1, 2, 1000, 4, 128, True),   # 250 rows per rank: ragged query and key tiles
+    (2, 3, 1000, 4, 64, True),
 ]
 
 
