@@ -1,13 +1,17 @@
 """Benchmark: one rank's share of context-parallel ring attention on one MI355X.
 
-A step is one pass of the whole hot path for the rank: zigzag-permute the
-global K and V (all ranks' shares, which the ring visits) and the rank's Q,
-run the rank's ring, and scatter O and lse back to global token order.  The
-ring is one launch that walks the N K/V blocks in ring order and folds each
-block into the running result by online softmax in registers
-(cpa_rank_forward_fused); `--ring partials` runs it as N partial-attention
-launches and N-1 merge launches instead (cpa_rank_forward).  Inputs are
-resident in HBM before timing starts.
+A step is one pass of the whole hot path for the rank: the zigzag layout's
+permute of Q/K/V into rank order, the rank's ring over all N K/V blocks with
+online-softmax folding, and O and lse back in global token order.  Modes:
+  --ring global   (default) one launch (cpa_share_forward): the kernel reads
+                  global-order Q/K/V and writes global-order O/lse, the zigzag
+                  permute folded into its addressing, the N blocks walked with
+                  the online-softmax state in registers;
+  --ring fused    explicit permutes to rank-major order, one fused ring launch
+                  (cpa_rank_forward_fused), inverse permutes;
+  --ring partials explicit permutes, N partial launches and N-1 merges
+                  (cpa_rank_forward), inverse permutes.
+Inputs are resident in HBM before timing starts.
 
 Metric: causal-useful attention TFLOP/s = 4 * D * B * H * P / t, where P is the
 number of (query, key) pairs the rank's queries may see (key position <= query
@@ -30,7 +34,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
 PEAK_HBM_GBS = 8000.0
-PMC_FILES = {"fused": os.path.join(ROOT, "profiles", "ring_fused_128k_pmc.json"),
+PMC_FILES = {"global": os.path.join(ROOT, "profiles", "ring_global_128k_pmc.json"),
+             "fused": os.path.join(ROOT, "profiles", "ring_fused_128k_pmc.json"),
              "partials": os.path.join(ROOT, "profiles", "partial_attn_128k_pmc.json")}
 KERNEL_SRC = os.path.join(ROOT, "sequence_attention_cpa_amd", "csrc", "partial_attn.hip")
 
@@ -117,8 +122,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="128k")
     ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--ring", choices=("fused", "partials"), default="fused",
-                    help="one fused launch per ring (default) or N partials + N-1 merges")
+    ap.add_argument("--ring", choices=("global", "fused", "partials"), default="global",
+                    help="global-layout ring launch (default), permutes + fused ring launch, or "
+                         "permutes + N partials + N-1 merges")
     ap.add_argument("--backward", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the rank's ring backward (reported under kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -145,9 +151,13 @@ def main():
     rank = args.rank
     Qh, Kh, Vh, _ = make_inputs(w)
     Q, K, V = Qh.to(dev), Kh.to(dev), Vh.to(dev)
-    fused = args.ring == "fused"
+    mfma_ok = w.dtype == "bf16" and w.D in (64, 128)
+    global_ok = mfma_ok and (w.C % 32 == 0)
+    if args.ring == "global" and not global_ok:
+        args.ring = "fused" if mfma_ok else "partials"
+    fused = args.ring in ("fused", "global")
     pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, dev, rank, rank + 1,
-                         fused=fused)
+                         fused=fused, global_layout=args.ring == "global")
     pos = pipe.pos_host.numpy()
     if w.causal:
         pairs = [causal_pairs(pos[rank], pos[j]) for j in range(w.N)]
@@ -180,9 +190,13 @@ def main():
     step_ms = np.array([evs_step[k].elapsed_time(evs_step[k + 1]) for k in range(args.steps)])
     ms_step_ev = float(step_ms.mean())
 
-    # Per-kernel timing on the same stream: the fused ring launch, the ring's
-    # partials (same kernel and arguments as inside cpa_rank_forward), its
-    # merges, and the K permute.
+    # Per-kernel timing on the same stream: the global-layout launch, the fused
+    # ring launch on rank-major data, the unfused ring's partials (same kernel
+    # and arguments as inside cpa_rank_forward), a merge, and the K permute.
+    zigzag = cpa.zigzag_permute
+    zigzag(K, pipe.pos, w.N, out=pipe.Kr)
+    zigzag(V, pipe.pos, w.N, out=pipe.Vr)
+    zigzag(Q, pipe.pos, w.N, rank_lo=rank, rank_hi=rank + 1, out=pipe.Qr)
     Lr = w.Lr
     tO = torch.empty((w.B, w.H, Lr, w.D), dtype=torch.float32, device=dev)
     tl = torch.empty((w.B, w.H, Lr), dtype=torch.float32, device=dev)
@@ -199,8 +213,13 @@ def main():
             evs.append((a, b))
         return evs
 
+    share_evs = []
+    if global_ok:
+        share_evs = timed(lambda: cpa.share_forward(Q, K, V, pos_d, w.N, w.causal,
+                                                    rank_lo=rank, rank_hi=rank + 1, out=pipe.O,
+                                                    lse=pipe.lse), reps)
     fused_evs, last_evs = [], []
-    if w.dtype == "bf16" and w.D in (64, 128):
+    if mfma_ok:
         fused_evs = timed(lambda: cpa.rank_forward_fused(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr,
                                                          pos_d, w.causal, out=tO, lse=tl), reps)
         # Balance: the last rank's ring does the same causal work under zigzag.
@@ -235,11 +254,17 @@ def main():
     p_avg_ms = float(p_ms.mean())
     f_ms = np.array([a.elapsed_time(b) for a, b in fused_evs]) if fused_evs else None
     o_ms = np.array([a.elapsed_time(b) for a, b in last_evs]) if last_evs else None
+    g_ms = np.array([a.elapsed_time(b) for a, b in share_evs]) if share_evs else None
 
     def stats(x):
         return {"median": round(float(np.median(x)), 4), "min": round(float(np.min(x)), 4),
                 "p90": round(float(np.percentile(x, 90)), 4)}
-    if fused:
+    if args.ring == "global":
+        dom_kernel = (f"partial_attn_mfma_kernel<{w.D}, global layout> (one launch, {w.N} K/V "
+                      "blocks)")
+        dom_ms = float(g_ms.mean())
+        dom_flop = useful
+    elif fused:
         dom_kernel = f"partial_attn_mfma_kernel<{w.D}> (one launch, {w.N} K/V blocks)"
         dom_ms = float(f_ms.mean())
         dom_flop = useful
@@ -286,6 +311,7 @@ def main():
                      "avg_launch_ms": round(dom_ms, 4), "useful_flop_per_launch": dom_flop},
         "kernels": {
             "ring": args.ring,
+            "global_ring_ms_stats": stats(g_ms) if g_ms is not None else None,
             "fused_ring_ms": round(float(f_ms.mean()), 4) if f_ms is not None else None,
             "fused_ring_ms_stats": stats(f_ms) if f_ms is not None else None,
             "fused_ring_ms_other_rank": ({"rank": other, **stats(o_ms)}

@@ -146,6 +146,27 @@ cpa_status cpa_rank_forward_fused(int32_t i, int32_t N, const void *Q_i, const v
                                   float scale, float *O_i, float *lse_i, void *stream);
 
 /*
+ * The ranks' rings directly on global-order data: cpa_rank_forward_fused for
+ * each rank r in [rank_lo, rank_hi), with the zigzag permute folded into the
+ * kernel's addressing (rank r's local row u is global row zig(r, u): chunk r
+ * for u < C, chunk 2N-1-r after, C = L/(2N)), so Q, K, V are read and O, lse
+ * written in global token order without separate permute passes ("序列与上下文
+ * 并行", 上下文并行 and 工程实践: the Z-shaped assignment, global positions).
+ *   Q, K, V    device [B, H, L, D] bf16, global order
+ *   pos_all    device int64 [N, L/N]: cpa_zigzag_layout(L, N)'s table
+ *              (precondition; it supplies the causal bounds)
+ *   O, lse     device float32 [B, H, L, D] / [B, H, L]: the selected ranks'
+ *              rows are written, the others are left untouched
+ *   causal, scale   as for cpa_partial
+ * bf16 with D = 64 or 128 and C a multiple of 32 (CPA_EUNSUPPORTED otherwise;
+ * use the permute + cpa_rank_forward_fused path).  One launch per rank.
+ */
+cpa_status cpa_share_forward(const void *Q, const void *K, const void *V, const int64_t *pos_all,
+                             cpa_dtype dt, int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+                             int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
+                             float *O, float *lse, void *stream);
+
+/*
  * Permutation between global order and rank-major zigzag order, for ranks
  * [rank_lo, rank_hi) (the data-pipeline step of "序列与上下文并行", 工程实践:
  * each rank's data must follow the CP layout).

@@ -12,7 +12,7 @@ from ._lib import (CPA_BF16, CPA_F32, CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED,  # no
                    CpaError, check, last_error, load, version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
-           "rank_forward_fused", "zigzag_permute", "rope", "zigzag_permute_rope",
+           "rank_forward_fused", "share_forward", "zigzag_permute", "rope", "zigzag_permute_rope",
            "backward_delta", "partial_backward", "rank_backward", "last_error",
            "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
 
@@ -125,6 +125,25 @@ def rank_forward_fused(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
     check(load().cpa_rank_forward_fused(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                         _dtype_code(Q_i), B, H, Lr * N, D, int(bool(causal)),
                                         float(scale), _ptr(out), _ptr(lse), _stream(Q_i)))
+    return out, lse
+
+
+def share_forward(Q, K, V, pos_all, N: int, causal: bool, scale: float = 0.0, rank_lo: int = 0,
+                  rank_hi: int | None = None, out=None, lse=None):
+    """Rings of ranks [rank_lo, rank_hi) on global-order Q/K/V [B,H,L,D] (bf16):
+    O [B,H,L,D] and lse [B,H,L] float32 in global order, the selected ranks'
+    rows written (the zigzag permute folded into the kernel's addressing)."""
+    torch = _torch()
+    rank_hi = N if rank_hi is None else rank_hi
+    B, H, L, D = Q.shape
+    if out is None:
+        out = torch.zeros((B, H, L, D), dtype=torch.float32, device=Q.device)
+    if lse is None:
+        lse = torch.full((B, H, L), float("-inf"), dtype=torch.float32, device=Q.device)
+    _need_gpu(Q, K, V, pos_all, out, lse)
+    check(load().cpa_share_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _dtype_code(Q), B, H,
+                                   L, D, N, rank_lo, rank_hi, int(bool(causal)), float(scale),
+                                   _ptr(out), _ptr(lse), _stream(Q)))
     return out, lse
 
 

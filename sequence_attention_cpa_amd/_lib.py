@@ -33,6 +33,8 @@ SIGNATURES = {
                                         _i64, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "cpa_rank_forward_fused": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
                                               _i32, _i64, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "cpa_share_forward": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32,
+                                         _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "cpa_zigzag_permute": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _i32,
                                           _i32, _i32, _i32, _vp]),
     "cpa_backward_delta": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i32, _vp, _vp]),

@@ -22,6 +22,14 @@ hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_al
                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
                             hipStream_t stream);
 
+// Rank i's whole ring in one launch on global-order data: Q, K, V [BH, N*Lr, D]
+// and O, lse [BH, N*Lr, ...] in global token order, rank r's local row u at
+// zigzag row zig(r, u); pos_all [N, Lr] is the zigzag table (used for the
+// causal bounds).  Requires Lr/2 % 32 == 0; writes only rank i's rows.
+hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, const int64_t* pos_all,
+                             float* O, float* lse, int BH, int64_t Lr, int N, int i, int D,
+                             bool causal, float scale, hipStream_t stream);
+
 // Partial attention, one query row per thread, fp32 arithmetic throughout
 // (fp32 inputs, and bf16 inputs with D = 16).
 hipError_t launch_partial_rowwise(const void* Q, const void* K, const void* V, bool bf16,

@@ -281,6 +281,38 @@ cpa_status cpa_zigzag_permute_rope(const void* src, void* dst, cpa_dtype dt, int
                   "permute+rope launch");
 }
 
+cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, const int64_t* pos_all,
+                             cpa_dtype dt, int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+                             int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
+                             float* O, float* lse, void* stream) {
+  if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (rank_lo < 0 || rank_hi > N || rank_lo >= rank_hi)
+    return fail(CPA_EINVAL, "rank range [%d, %d) invalid for N=%d", rank_lo, rank_hi, N);
+  const int64_t Lr = L / N;
+  if (dt != CPA_BF16 || (D != 64 && D != 128))
+    return fail(CPA_EUNSUPPORTED, "the global-layout ring runs bf16 with D = 64 or 128");
+  if ((Lr / 2) % 32 != 0)
+    return fail(CPA_EUNSUPPORTED, "the global-layout ring needs chunks L/(2N) that are multiples "
+                                  "of 32 (L=%lld, N=%d); use the rank-major path",
+                (long long)L, N);
+  if (Lr > ((int64_t)1 << 30)) return fail(CPA_ESHAPE, "L/N is limited to 2^30 rows");
+  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if (!Q || !K || !V || !pos_all || !O || !lse) return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(CPA_EINVAL, "Q, K, V and O must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(pos_all, 8))
+    return fail(CPA_EINVAL, "lse must be 4-byte and pos_all 8-byte aligned");
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
+  for (int32_t r = rank_lo; r < rank_hi; ++r) {
+    const hipError_t e = cpa::launch_share_mfma(Q, K, V, pos_all, O, lse, B * H, Lr, N, r, D,
+                                                causal != 0, scale, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e, "global-layout ring launch");
+  }
+  return ok();
+}
+
 cpa_status cpa_backward_delta(const float* O, const void* dO, cpa_dtype dt, int64_t rows,
                               int32_t D, float* delta, void* stream) {
   if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);

@@ -78,7 +78,13 @@ constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold (log2 units)
 // head sweep those blocks in step and share each K/V tile through L2; only
 // the own block gives every tile a different causal prefix, after which the
 // workgroups no longer run in step.
-template <int D>
+//
+// GL (global layout): Q, K, V, O and lse are the whole sequence in global
+// token order, [BH, N * Lq, ...], and rank r's local row u lives at global row
+// zig(r, u) of the zigzag layout (chunk r for u < Lq/2, chunk 2N-1-r after),
+// so the zigzag permute is folded into the addressing.  The chunk length
+// Lq/2 is a multiple of 32, so every 32-row tile is contiguous in memory.
+template <int D, bool GL>
 __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ O,
@@ -106,9 +112,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   const int64_t qrow = q_base + wv * 32 + l32;
   const int64_t qrow_c = qrow < Lq ? qrow : Lq - 1;
 
-  const __bf16* Qbh = Q + (int64_t)bh * Lq * D;
-  float* Obh = O + (int64_t)bh * Lq * D;
-  float* lse_bh = lse + (int64_t)bh * Lq;
+  const int64_t C = Lq / 2;                 // chunk length (GL)
+  const int64_t Lrow = GL ? Lq * nblk : Lq;  // rows per head in Q / O / lse
+  // global row of rank r's local row u (GL)
+  auto zig = [&](int r, int64_t u) __attribute__((always_inline)) -> int64_t {
+    const bool lo = u < C;
+    return (lo ? r : 2 * nblk - 1 - r) * C + (lo ? u : u - C);
+  };
+  const __bf16* Qbh = Q + (int64_t)bh * Lrow * D;
+  float* Obh = O + (int64_t)bh * Lrow * D;
+  float* lse_bh = lse + (int64_t)bh * Lrow;
   const int64_t q_first = causal ? q_off[q_base] : 0;
   const int64_t q_last = causal ? q_off[last_row] : 0;
   const int64_t my_qpos = causal ? q_off[qrow_c] : 0;
@@ -127,7 +140,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = *reinterpret_cast<const bf16x8*>(Qbh + qrow_c * D + kk * 16 + hi * 8);
+    qf[kk] = *reinterpret_cast<const bf16x8*>(Qbh + (GL ? zig(first, qrow_c) : qrow_c) * D +
+                                              kk * 16 + hi * 8);
   // K operand of (kb, kk): tile row kb*32 + l32, logical chunk kk*2 + hi.
   int koff[KK];
 #pragma unroll
@@ -154,10 +168,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     coff[i] = crow[i] * RB + swz<D>(crow[i], lane % G::CHUNKS) * 16;
   }
 
-  auto copy_tile = [&](const __bf16* src, int j, lds_char* dst) __attribute__((always_inline)) {
+  // GL: a block's rows below C come from the first chunk (base src), the
+  // rest from the second (base src_hi, already offset by -C rows).
+  const __bf16* Kbh_hi = nullptr;
+  const __bf16* Vbh_hi = nullptr;
+  auto copy_tile = [&](const __bf16* src, const __bf16* src_hi, int j, lds_char* dst)
+                       __attribute__((always_inline)) {
     const int64_t u0 = (int64_t)j * BN;
     if (u0 + BN <= Lk) {
-      const __bf16* base = src + u0 * D;
+      const __bf16* base = ((GL && u0 >= C) ? src_hi : src) + u0 * D;
 #pragma unroll
       for (int i = 0; i < G::IPW; ++i)
         copy16_saddr((uint32_t)coff[i], base, lds_addr(dst + (wv * G::IPW + i) * 1024));
@@ -241,8 +260,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     constexpr int P = decltype(P_)::value;
     constexpr bool HAS_PV = decltype(PV_)::value;
     constexpr bool HAS_QK = decltype(QK_)::value;
-    if (t + 2 < T) copy_tile(Kbh, t + 2, Kl + P * TB);
-    copy_tile(Vbh, t, Vl + P * TB);
+    if (t + 2 < T) copy_tile(Kbh, Kbh_hi, t + 2, Kl + P * TB);
+    copy_tile(Vbh, Vbh_hi, t, Vl + P * TB);
 
     const float m_use = m2 == -INFINITY ? 0.f : m2;
     const lds_char* Kt = Kl + (P ^ 1) * TB;  // K(t+1)
@@ -313,8 +332,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
 
   for (int sb = 0; sb < nblk; ++sb) {
   const int blk = (first + 1 + sb) % nblk;
-  Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
-  Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
+  if constexpr (GL) {
+    const int64_t lo_row = (int64_t)blk * C, hi_row = (int64_t)(2 * nblk - 1 - blk) * C - C;
+    Kbh = K + ((int64_t)bh * Lrow + lo_row) * D;
+    Vbh = V + ((int64_t)bh * Lrow + lo_row) * D;
+    Kbh_hi = K + ((int64_t)bh * Lrow + hi_row) * D;
+    Vbh_hi = V + ((int64_t)bh * Lrow + hi_row) * D;
+  } else {
+    Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
+    Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
+    Kbh_hi = Kbh;
+    Vbh_hi = Vbh;
+  }
   if (causal) {
     const int64_t* kb_off = k_off + blk * koff_stride;
     n_lo = (int)count_le(kb_off, Lk, q_first);
@@ -330,8 +359,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   T = (n_hi + BN - 1) / BN;
 
   // Prologue: K(0), K(1) into LDS; scores of tile 0.
-  copy_tile(Kbh, 0, Kl);
-  if (T > 1) copy_tile(Kbh, 1, Kl + TB);
+  copy_tile(Kbh, Kbh_hi, 0, Kl);
+  if (T > 1) copy_tile(Kbh, Kbh_hi, 1, Kl + TB);
   wait_copies();
   __syncthreads();
 #pragma unroll
@@ -390,7 +419,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   const float ltot_f = xhalf_sum((lsum_f4[0] + lsum_f4[1]) + (lsum_f4[2] + lsum_f4[3]));
   if (qrow < Lq) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float* orow = Obh + qrow * D;
+    const int64_t orow_i = GL ? zig(first, qrow) : qrow;
+    float* orow = Obh + orow_i * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -399,13 +429,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
                           acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
         *reinterpret_cast<float4*>(orow + db * 32 + gq * 8 + hi * 4) = v;
       }
-    if (hi == 0) lse_bh[qrow] = ltot_f > 0.f ? (m2 + __log2f(ltot_f)) * LN2 : -INFINITY;
+    if (hi == 0) lse_bh[orow_i] = ltot_f > 0.f ? (m2 + __log2f(ltot_f)) * LN2 : -INFINITY;
   }
 }
 
 }  // namespace
 
 namespace {
+template <bool GL>
 hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int64_t* q_off,
                          const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
                          int64_t Lk, int64_t kv_stride, int64_t koff_stride, int nblk, int first,
@@ -414,12 +445,12 @@ hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int6
   const dim3 grid((unsigned)(n_qtiles * BH));
   const float c_log2 = scale * LOG2E;
   if (D == 128) {
-    hipLaunchKernelGGL(partial_attn_mfma_kernel<128>, grid, dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((partial_attn_mfma_kernel<128, GL>), grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
                        BH, Lq, Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0, c_log2,
                        n_qtiles);
   } else {
-    hipLaunchKernelGGL(partial_attn_mfma_kernel<64>, grid, dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((partial_attn_mfma_kernel<64, GL>), grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
                        BH, Lq, Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0, c_log2,
                        n_qtiles);
@@ -431,16 +462,23 @@ hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int6
 hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V, const int64_t* q_off,
                                const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
                                int64_t Lk, int D, bool causal, float scale, hipStream_t stream) {
-  return launch_blocks(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, 0, 0, 1, 0, D, causal, scale,
-                       stream);
+  return launch_blocks<false>(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, 0, 0, 1, 0, D, causal,
+                              scale, stream);
 }
 
 hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_all,
                             const int64_t* q_off, const int64_t* pos_all, float* O, float* lse,
                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
                             hipStream_t stream) {
-  return launch_blocks(Q_i, K_all, V_all, q_off, pos_all, O, lse, BH, Lr, Lr, (int64_t)BH * Lr * D,
-                       Lr, N, i, D, causal, scale, stream);
+  return launch_blocks<false>(Q_i, K_all, V_all, q_off, pos_all, O, lse, BH, Lr, Lr,
+                              (int64_t)BH * Lr * D, Lr, N, i, D, causal, scale, stream);
+}
+
+hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, const int64_t* pos_all,
+                             float* O, float* lse, int BH, int64_t Lr, int N, int i, int D,
+                             bool causal, float scale, hipStream_t stream) {
+  return launch_blocks<true>(Q, K, V, pos_all + (int64_t)i * Lr, pos_all, O, lse, BH, Lr, Lr, 0,
+                             Lr, N, i, D, causal, scale, stream);
 }
 
 }  // namespace cpa

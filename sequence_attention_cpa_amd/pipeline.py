@@ -11,6 +11,11 @@ With `fused=True` each rank's ring is one launch (cpa_rank_forward_fused:
 the online-softmax state stays in registers across the N blocks) instead of
 N partial launches and N-1 merges; bf16 with D = 64 or 128 only.
 
+With `global_layout=True` the whole step is one cpa_share_forward call per
+rank: the kernel reads global-order Q/K/V and writes global-order O/lse,
+with the zigzag permute folded into its addressing (bf16, D = 64 or 128,
+chunks L/(2N) a multiple of 32, no RoPE).
+
 With `rope_base` set, Q and K are rotated at their global positions on the
 way into rank-major order (cpa_zigzag_permute_rope: the rotary embedding is
 folded into the permute, so it costs no extra pass over memory).
@@ -27,19 +32,23 @@ use); `step` and `backward` allocate nothing after that.
 from __future__ import annotations
 
 from . import (CPA_ROPE_INTERLEAVED, rank_backward, rank_forward, rank_forward_fused,
-               rank_forward_workspace, zigzag_layout, zigzag_permute, zigzag_permute_rope)
+               rank_forward_workspace, share_forward, zigzag_layout, zigzag_permute,
+               zigzag_permute_rope)
 
 
 class SharePipeline:
     def __init__(self, B: int, H: int, L: int, D: int, N: int, causal: bool, dtype, device,
                  rank_lo: int = 0, rank_hi: int | None = None, scale: float = 0.0,
                  fused: bool = False, rope_base: float | None = None,
-                 rope_pairing: int = CPA_ROPE_INTERLEAVED):
+                 rope_pairing: int = CPA_ROPE_INTERLEAVED, global_layout: bool = False):
         import torch
 
         self.B, self.H, self.L, self.D, self.N = B, H, L, D, N
         self.causal, self.scale, self.fused = causal, scale, fused
         self.rope_base, self.rope_pairing = rope_base, rope_pairing
+        self.global_layout = global_layout
+        if global_layout and rope_base is not None:
+            raise ValueError("the global-layout step has no RoPE; rotate Q/K first (cpa_rope)")
         self.rank_lo = rank_lo
         self.rank_hi = N if rank_hi is None else rank_hi
         nr = self.rank_hi - self.rank_lo
@@ -60,6 +69,11 @@ class SharePipeline:
         """Q, K, V: global [B, H, L, D] on the device.  Returns global (O, lse);
         rows of ranks outside [rank_lo, rank_hi) are left as initialised."""
         N, lo, hi = self.N, self.rank_lo, self.rank_hi
+        if self.global_layout:
+            self._inputs = (Q, K, V)
+            share_forward(Q, K, V, self.pos, N, self.causal, self.scale, lo, hi, out=self.O,
+                          lse=self.lse)
+            return self.O, self.lse
         if self.rope_base is None:
             zigzag_permute(K, self.pos, N, out=self.Kr)
             zigzag_permute(Q, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Qr)
@@ -100,6 +114,13 @@ class SharePipeline:
             self.dQ = torch.zeros((self.B, self.H, self.L, self.D), **f32)
             self.dK = torch.empty_like(self.dQ)
             self.dV = torch.empty_like(self.dQ)
+        if self.global_layout:  # the ring backward works on rank-major data
+            Q, K, V = self._inputs
+            zigzag_permute(K, self.pos, N, out=self.Kr)
+            zigzag_permute(V, self.pos, N, out=self.Vr)
+            zigzag_permute(Q, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Qr)
+            zigzag_permute(self.O, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Or)
+            zigzag_permute(self.lse, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.lser)
         zigzag_permute(dO, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.dOr)
         self.dKr.zero_()
         self.dVr.zero_()

@@ -349,3 +349,29 @@ def _rbwd(lib, **kw):
 def test_rank_backward_rejects(lib, kw, status):
     assert _rbwd(lib, **kw) == status
     assert cpa.last_error() != ""
+
+
+def _share(lib, **kw):
+    a = dict(Q=P, K=P, V=P, pos=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128, N=4, lo=0, hi=4,
+             causal=1, scale=0.0, O=P, lse=P, stream=None)
+    a.update(kw)
+    return lib.cpa_share_forward(a["Q"], a["K"], a["V"], a["pos"], a["dt"], a["B"], a["H"], a["L"],
+                                 a["D"], a["N"], a["lo"], a["hi"], a["causal"], a["scale"],
+                                 a["O"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=500), _lib.CPA_ESHAPE),
+    (dict(L=128), _lib.CPA_EUNSUPPORTED),      # chunks of 16 keys: not a multiple of 32
+    (dict(L=1000), _lib.CPA_EUNSUPPORTED),     # chunk 125: not a multiple of 32
+    (dict(dt=_lib.CPA_F32), _lib.CPA_EUNSUPPORTED),
+    (dict(D=16), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=6), _lib.CPA_EDTYPE),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(lo=2, hi=1), _lib.CPA_EINVAL),
+    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(O=P + 4), _lib.CPA_EINVAL),
+])
+def test_share_forward_rejects(lib, kw, status):
+    assert _share(lib, **kw) == status
+    assert cpa.last_error() != ""

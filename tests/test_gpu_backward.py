@@ -107,7 +107,8 @@ def test_partial_backward(case):
 
 def run_pipeline(Q, K, V, dO, N, causal, fused, rope=None):
     B, H, L, D = Q.shape
-    pipe = SharePipeline(B, H, L, D, N, causal, Q.dtype, DEV, fused=fused, rope_base=rope)
+    pipe = SharePipeline(B, H, L, D, N, causal, Q.dtype, DEV, fused=fused == True,
+                         rope_base=rope, global_layout=fused == "global")
     pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     dQ, dK, dV = pipe.backward(dO.to(DEV))
     torch.cuda.synchronize()
@@ -122,6 +123,7 @@ RANK_BWD_CASES = [
     (torch.bfloat16, 1, 2, 1536, 4, 128, False, True),
     (torch.bfloat16, 1, 2, 2048, 1, 128, True, True),
     (torch.bfloat16, 1, 2, 256, 16, 128, True, True),   # chunks of 8: every tile masked
+    (torch.bfloat16, 2, 2, 2048, 4, 128, True, "global"),  # forward step on global layout
     (torch.bfloat16, 1, 2, 1000, 4, 128, True, True),   # 250 rows per rank: ragged tiles
     (torch.bfloat16, 2, 3, 1000, 4, 64, True, True),
     (torch.float32, 1, 2, 64, 4, 16, True, False),      # the fp32 tiny shape

@@ -257,8 +257,9 @@ def test_permute_bit_exact(dtype, D, ranks):
 
 # ------------------------------------------------------------ rank forward
 
-def stitched_all_ranks(w, Q, K, V, fused=False):
-    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=fused)
+def stitched_all_ranks(w, Q, K, V, fused=False, global_layout=False):
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=fused,
+                         global_layout=global_layout)
     O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     torch.cuda.synchronize()
     return O.cpu().double().numpy(), lse.cpu().double().numpy()
@@ -287,6 +288,7 @@ def test_rank_forward_12k_all_ranks_every_row():
     Q, K, V, _ = make_inputs(w)
     say("12k: GPU")
     outs = {f: stitched_all_ranks(w, Q, K, V, f) for f in (False, True)}
+    outs["global"] = stitched_all_ranks(w, Q, K, V, True, global_layout=True)
     say("12k: oracle")
     rows = {(b, h): np.arange(w.L) for b in range(w.B) for h in range(w.H)}
     ref = oracle_rows(lambda b, h: widen(Q[b, h]), lambda b, h: widen(K[b, h]),
@@ -305,10 +307,11 @@ def share_check(name, rank, n_rows, block):
     Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
     results = {}
     pos = None
-    for fused in (False, True):
+    modes = (False, True, "global")
+    for fused in modes:
         say(f"{name}: GPU rank {rank} fused={fused}")
         pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, rank, rank + 1,
-                             fused=fused)
+                             fused=bool(fused), global_layout=fused == "global")
         Od, lsed = pipe.step(Qd, Kd, Vd)
         pos = pipe.pos_host.numpy()
         if "g" not in results:
@@ -325,7 +328,7 @@ def share_check(name, rank, n_rows, block):
                       lambda b, h: widen(V[b, h]), rows, w.causal, block=block)
     Or = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
     lr = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
-    for fused in (False, True):
+    for fused in modes:
         O, lse = results[fused]
         mx, mean = assert_bf16_close(O, lse, Or, lr, f"{name} fused={fused}")
         say(f"{name} fused={fused}: max {mx:.3e} mean {mean:.3e}")
@@ -367,3 +370,40 @@ def test_rank_forward_fused_small_shapes(case):
     O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     torch.cuda.synchronize()
     assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
+
+
+SHARE_CASES = [c for c in FUSED_CASES if (c[2] // c[3] // 2) % 32 == 0]
+
+
+@pytest.mark.parametrize("case", SHARE_CASES, ids=[str(c) for c in SHARE_CASES])
+def test_share_forward_global_layout(case):
+    """The global-layout ring (zigzag permute folded into the kernel) equals
+    the oracle for every rank; rows are read and written in global order."""
+    B, H, L, N, D, causal = case
+    Q = rand((B, H, L, D), torch.bfloat16, 63)
+    K = rand((B, H, L, D), torch.bfloat16, 64)
+    V = rand((B, H, L, D), torch.bfloat16, 65)
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), causal)
+    pipe = SharePipeline(B, H, L, D, N, causal, Q.dtype, DEV, fused=True, global_layout=True)
+    O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
+    torch.cuda.synchronize()
+    assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
+
+
+def test_share_forward_rank_subset_leaves_other_rows():
+    """Only the selected ranks' rows are written."""
+    B, H, L, N, D = 1, 2, 2048, 4, 128
+    Q, K, V = (rand((B, H, L, D), torch.bfloat16, 66 + i).to(DEV) for i in range(3))
+    pos = cpa.zigzag_layout(L, N)
+    O = torch.full((B, H, L, D), 7.0, device=DEV)
+    lse = torch.full((B, H, L), 7.0, device=DEV)
+    cpa.share_forward(Q, K, V, pos.to(DEV), N, True, rank_lo=1, rank_hi=3, out=O, lse=lse)
+    torch.cuda.synchronize()
+    mine = np.concatenate([pos[1].numpy(), pos[2].numpy()])
+    other = np.setdiff1d(np.arange(L), mine)
+    assert torch.all(O[:, :, torch.from_numpy(other).to(DEV)] == 7.0)
+    assert torch.all(lse[:, :, torch.from_numpy(other).to(DEV)] == 7.0)
+    Or, lr = cpa_oracle.attention(widen(Q.cpu()), widen(K.cpu()), widen(V.cpu()), True)
+    gi = torch.from_numpy(mine).to(DEV)
+    assert_bf16_close(O[:, :, gi].cpu().double().numpy(), lse[:, :, gi].cpu().double().numpy(),
+                      Or[:, :, mine], lr[:, :, mine], "ranks 1-2")
