@@ -20,22 +20,21 @@
 //    straight from the score registers; V^T comes from row-major V in LDS
 //    through ds_read_b64_tr_b16.
 //  * Software pipeline: iteration t issues the matrix work of PV(t-1) and
-//    QK^T(t+1) together with the exponentials of tile t in one straight-line
-//    block, so the wave's own VALU work can issue in the shadow of its MFMAs
-//    (operands are fetched four MFMAs ahead).  Only the row max of tile t+1
-//    and the rare rescale run between the matrix phases.  (Pinning the
-//    interleave with sched_group_barrier measured slower than the compiler's
-//    own schedule.)
+//    QK^T(t+1), then the exponentials of tile t, the row max of tile t+1 and
+//    the rare rescale.  The operand reads from LDS run six MFMAs ahead of
+//    their use; sched_group_barrier pins only that order of LDS reads and
+//    MFMAs (pinning the VALU work between the MFMAs as well measured slower).
 //  * K and V tiles of 32 keys live in two LDS buffers each.  Iteration t
 //    starts the copies of K(t+2) and V(t) straight from global memory into
 //    LDS (global_load_lds_dwordx4, no staging registers; offsets precomputed
 //    per lane, base in SGPRs) and waits for them at its end.  The copy is
 //    issued from inline asm so the compiler does not make every LDS read wait
-//    for it.  A 16-byte XOR swizzle keeps both operand read patterns free of
-//    bank conflicts; all operand addresses are per-lane constants plus
-//    immediate offsets.
+//    for it.  The tile is stored in column blocks of 64 or 128 bytes with a
+//    16-byte XOR inside each block (lds_slot): every operand read is one of a
+//    few per-lane bases plus an immediate offset, and no read has bank
+//    conflicts.  Each copy instruction writes 1 KiB of LDS contiguously.
 //  * Softmax rescaling is lazy and exact: the exponent reference is an integer
-//    (log2 units) raised only when a row's max grows by more than 2^8; the
+//    (log2 units) raised only when a row's max grows by more than 2^32; the
 //    rescale is then a power of two, applied with ldexp to O, l and the P of
 //    the tile already computed but not yet multiplied into O.  O is divided by
 //    the sum of the packed bf16 P (v_dot2_f32_bf16), i.e. exactly the weights
@@ -62,10 +61,15 @@ using namespace tile;
 
 constexpr int BM = 128;        // query rows per workgroup
 constexpr int NKB = BN / 32;   // 32-key MFMA blocks per tile
+static_assert(NKB == 1, "the LDS tile layout holds 32 rows");
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold (log2 units)
+// Lazy-rescale threshold (log2 units).  P stays below 2^33, exact in bf16
+// and fp32 (their precision is relative), and the fp32 accumulators stay far
+// from overflow for any |V| below 2^60 / keys; 2^8 measured 2 % slower on
+// inputs with outlier rows, which rescale often.
+constexpr float RESCALE_LOG2 = 32.0f;
 
 // Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
 // K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
@@ -84,6 +88,24 @@ constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold (log2 units)
 // zig(r, u) of the zigzag layout (chunk r for u < Lq/2, chunk 2N-1-r after),
 // so the zigzag permute is folded into the addressing.  The chunk length
 // Lq/2 is a multiple of 32, so every 32-row tile is contiguous in memory.
+// LDS layout of a 32-row K or V tile, in 16-byte slots, with column blocks
+// of W chunks (W = 4: 64-byte blocks, W = 8: 128-byte blocks): logical chunk
+// c of row r sits at slot 32W*(c/W) + W*r + ((c%W) ^ key(r)).  Column blocks
+// keep every operand read at one of a few per-lane bases plus a compile-time
+// offset; the XOR key spreads each 16-lane phase of the K reads and each
+// 32-lane half of the transposing V reads over distinct banks.  Copy
+// instruction n fills slots [64n, 64n + 64): 16 rows x 64 bytes of the tile
+// (W = 4) or 8 rows x 128 bytes, whole cache lines (W = 8).
+template <int W>
+__device__ __forceinline__ int lds_key(int r) {
+  if constexpr (W == 4) return (r >> 2) & 3;
+  else return (((r >> 1) & 1) ? 5 : 0) ^ (((r >> 2) & 1) ? 2 : 0) ^ (((r >> 3) & 1) ? 4 : 0);
+}
+template <int W>
+__device__ __forceinline__ int lds_slot(int r, int c) {
+  return 32 * W * (c / W) + W * r + ((c % W) ^ lds_key<W>(r));
+}
+
 template <int D, bool GL>
 __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -95,6 +117,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   constexpr int RB = G::ROW_BYTES;
   constexpr int KK = G::KK;
   constexpr int DB = G::DB;
+  // Column-block width of the LDS tile layout, in 16-byte chunks.  The
+  // global-order instantiation copies whole 128-byte lines (W = 8): there the
+  // half-line copies of W = 4 measured 5-7 % slower, bound by copy latency.
+  // The rank-major one runs faster with W = 4, which needs fewer base
+  // registers.
+  constexpr int W = GL ? 8 : 4;
+  constexpr int KB = W / 2;     // K operand base registers
+  constexpr int BLK = 512 * W;  // bytes per column block of a tile
   __shared__ __attribute__((aligned(1024))) char k_lds_raw[2 * TB];
   __shared__ __attribute__((aligned(1024))) char v_lds_raw[2 * TB];
   lds_char* const Kl = (lds_char*)k_lds_raw;
@@ -142,30 +172,36 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   for (int kk = 0; kk < KK; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(Qbh + (GL ? zig(first, qrow_c) : qrow_c) * D +
                                               kk * 16 + hi * 8);
-  // K operand of (kb, kk): tile row kb*32 + l32, logical chunk kk*2 + hi.
-  int koff[KK];
+  // K operand of kk: tile row l32, logical chunk kk*2 + hi, at byte
+  // (kk / KB) * BLK + kbase[kk % KB] of the tile.
+  int kbase[KB];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) koff[kk] = l32 * RB + swz<D>(l32, kk * 2 + hi) * 16;
-  // V operand of (kb, half, db): two transposing reads of rows
-  // kb*32 + half*16 + vrow (+8), 8 bytes inside chunk db*4 + vch.
+  for (int e = 0; e < KB; ++e) kbase[e] = lds_slot<W>(l32, e * 2 + hi) * 16;
+  // V operand of (half, db): two transposing reads (p = 0, 1) of rows
+  // half*16 + vrow + 8p, 8 bytes inside chunk db*4 + vch, at byte
+  // vaddr(half, db, p) of the tile.
   const int vrow = hi * 4 + ((lane & 15) >> 2);
   const int vch = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
   const int vsub = (lane & 1) * 8;
-  int voff[DB][2];
+  int vbase[2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      voff[db][p] = (vrow + 8 * p) * RB + swz<D>(vrow + 8 * p, db * 4 + vch) * 16 + vsub;
-  // Copy instruction i of this wave fills tile rows (wv*IPW + i)*RPI + ...:
-  // lane takes physical chunk lane % CHUNKS of its row.
+  for (int e = 0; e < 2; ++e)
+    vbase[e] = (W == 4 ? lds_slot<W>(vrow + 8 * e, vch) : lds_slot<W>(vrow, 4 * e + vch)) * 16 +
+               vsub;
+  auto vaddr = [&](int half, int db, int p) __attribute__((always_inline)) -> int {
+    if constexpr (W == 4) return half * 1024 + db * 2048 + vbase[p];
+    else return half * 2048 + (db >> 1) * 4096 + p * 1024 + vbase[p ^ (db & 1)];
+  };
+  // Copy instruction n = wv*IPW + i fills LDS bytes [1024 n, 1024 n + 1024):
+  // lane takes the 16-byte piece whose slot is 64 n + lane.
   int coff[G::IPW];
   int crow[G::IPW];
 #pragma unroll
   for (int i = 0; i < G::IPW; ++i) {
     const int n = wv * G::IPW + i;
-    crow[i] = n * G::RPI + lane / G::CHUNKS;
-    coff[i] = crow[i] * RB + swz<D>(crow[i], lane % G::CHUNKS) * 16;
+    crow[i] = (64 / W) * (n % (W / 2)) + lane / W;
+    const int c = W * (n / (W / 2)) + ((lane % W) ^ lds_key<W>(crow[i]));
+    coff[i] = crow[i] * RB + c * 16;
   }
 
   // GL: a block's rows below C come from the first chunk (base src), the
@@ -175,18 +211,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
   auto copy_tile = [&](const __bf16* src, const __bf16* src_hi, int j, lds_char* dst)
                        __attribute__((always_inline)) {
     const int64_t u0 = (int64_t)j * BN;
+    const __bf16* base = ((GL && u0 >= C) ? src_hi : src) + u0 * D;
     if (u0 + BN <= Lk) {
-      const __bf16* base = ((GL && u0 >= C) ? src_hi : src) + u0 * D;
 #pragma unroll
       for (int i = 0; i < G::IPW; ++i)
         copy16_saddr((uint32_t)coff[i], base, lds_addr(dst + (wv * G::IPW + i) * 1024));
-    } else {  // last, ragged tile: rows past the block re-read the last row (masked later)
+    } else {  // last, ragged tile: rows past the block re-read its last row (masked later)
+      const int last = (int)(Lk - 1 - u0);  // last valid tile row, 0 .. BN-2
 #pragma unroll
       for (int i = 0; i < G::IPW; ++i) {
-        int64_t u = u0 + crow[i];
-        u = u < Lk ? u : Lk - 1;
-        const char* g = (const char*)(src + u * D) + (coff[i] - crow[i] * RB);
-        copy16_vaddr(g, lds_addr(dst + (wv * G::IPW + i) * 1024));
+        const int over = crow[i] - last;  // rows past the end: move back by that many
+        copy16_saddr((uint32_t)(coff[i] - (over > 0 ? over : 0) * RB), base,
+                     lds_addr(dst + (wv * G::IPW + i) * 1024));
       }
     }
   };
@@ -269,21 +305,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     constexpr int NV = HAS_PV ? 2 * NKB * DB : 0;
     constexpr int NQ = HAS_QK ? NKB * KK : 0;
     constexpr int NM = NV + NQ;
-    constexpr int PF = 4;  // operands in flight ahead of the MFMA using them
+    // operands in flight ahead of the MFMA using them (chosen by measurement
+    // for each layout)
+    constexpr int PF = GL ? 4 : 6;
     auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
       if (i < NV) {
         const int kb = i / (2 * DB), half = (i / DB) & 1, db = i % DB;
-        const lds_char* b = Vt + (kb * 32 + half * 16) * RB;
         const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(b + voff[db][0]));
+            (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 0)));
         const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(b + voff[db][1]));
+            (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 1)));
         const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         return __builtin_bit_cast(bf16x8, v8);
       }
       const int q = i - NV, kb = q / KK, kk = q % KK;
       return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
-          Kt + kb * 32 * RB + koff[kk]);
+          Kt + (kk / KB) * BLK + kbase[kk % KB]);
     };
     bf16x8 ob[PF];
 #pragma unroll
@@ -300,6 +337,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
         const int q = i - NV, kb = q / KK, kk = q % KK;
         s[P ^ 1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             cur, qf[kk], kk == 0 ? zero16 : s[P ^ 1][kb], 0, 0, 0);
+      }
+    }
+    // Keep the operand reads PF MFMAs ahead in the final schedule as well: left
+    // alone, the scheduler sinks each LDS read down to the MFMA that uses it.
+#pragma unroll
+    for (int i = 0; i < PF && i < NM; ++i) {
+      if (i < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads (V)
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // 1 LDS read (K)
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA i
+      if (i + PF < NM) {
+        if (i + PF < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     // exp2 of tile t, packed to bf16; row sums of the fp32 and of the packed values.
@@ -368,8 +420,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(Kl + kb * 32 * RB +
-                                                                             koff[kk]),
+          *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+              Kl + (kk / KB) * BLK + kbase[kk % KB]),
           qf[kk], kk == 0 ? zero16 : s[0][kb], 0, 0, 0);
   finish_scores(0, s[0], pf[0], std::false_type{});
   __syncthreads();  // K(0) is read; its buffer is refilled by iteration 0
@@ -401,11 +453,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const lds_char* b = Vt + (kb * 32 + half * 16) * RB;
           const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(b + voff[db][0]));
+              (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 0)));
           const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(b + voff[db][1]));
+              (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 1)));
           const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
                                                             pf[P][kb][half], acc[db], 0, 0, 0);

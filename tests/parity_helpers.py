@@ -55,6 +55,15 @@ def host_threads():
     return max(1, min(n, 16))
 
 
+def host_map(fn, items):
+    """list(map(fn, items)) over host threads, one BLAS thread per worker: the
+    workers already use every core, and a multi-threaded BLAS inside each of
+    them oversubscribes the host (measured 45x slower on the 12k oracle)."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1), ThreadPoolExecutor(host_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
 def widen(t):
     """Exact widening of a bf16/fp32 tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
@@ -96,5 +105,4 @@ def oracle_rows(Q64, K64, V64, rows_by_bh, causal, scale=None, block=64):
         q = Q64(b, h)[rows]
         return bh, cpa_oracle.attention_rows(q, rows, K64(b, h), V64(b, h), causal, scale,
                                              block=block)
-    with ThreadPoolExecutor(host_threads()) as ex:
-        return dict(ex.map(one, list(rows_by_bh)))
+    return dict(host_map(one, list(rows_by_bh)))

@@ -2,14 +2,13 @@
 cpa_rank_backward and the pipeline's backward) against the fp64 oracle,
 through the C ABI."""
 import sys
-from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 import torch
 
 from oracle import cpa_oracle
-from parity_helpers import assert_grad_close, host_threads, widen
+from parity_helpers import assert_grad_close, host_map, widen
 
 import sequence_attention_cpa_amd as cpa
 from sequence_attention_cpa_amd.pipeline import SharePipeline
@@ -154,8 +153,7 @@ def oracle_backward_heads(Q, K, V, dO, heads, causal=True):
         O, lse = cpa_oracle.attention_rows(q, pos, k, v, causal)
         delta = cpa_oracle.backward_delta(O, g)
         return bh, cpa_oracle.backward_rows(q, pos, k, v, g, lse, delta, causal)
-    with ThreadPoolExecutor(host_threads()) as ex:
-        return dict(ex.map(one, heads))
+    return dict(host_map(one, heads))
 
 
 def test_ring_backward_12k_eight_heads_every_row():
@@ -211,8 +209,7 @@ def test_ring_backward_128k_sampled():
                                              cpa_oracle.backward_delta(Ot, g[tail]), True,
                                              block=32)
         return h, dq, dk[tail], dv[tail]
-    with ThreadPoolExecutor(host_threads()) as ex:
-        res = dict((h, (a, b, c)) for h, a, b, c in ex.map(one, range(w.H)))
+    res = dict((h, (a, b, c)) for h, a, b, c in host_map(one, range(w.H)))
     for n, (name, got) in enumerate((("dQ", dQs), ("dK", dKs), ("dV", dVs))):
         r = np.stack([res[h][n] for h in range(w.H)])[None]
         e = assert_grad_close(got, r, True, f"128k {name}")
