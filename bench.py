@@ -238,16 +238,30 @@ def main():
     pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr), reps)
     rope_evs = timed(lambda: cpa.zigzag_permute_rope(K, pos_d, w.N, 10000.0, out=pipe.Kr), reps)
     # Ring backward of the same rank (delta + dQ pass + dK/dV pass), after a
-    # forward step so that O and lse are the ring's.
-    bwd_evs = []
+    # forward step so that O and lse are the ring's: on global-order data
+    # (cpa_share_backward, the pipeline's backward in the default mode) and on
+    # rank-major copies of the same tensors (cpa_rank_backward).
+    bwd_evs, gbwd_evs = [], []
     if args.backward:
         pipe.step(Q, K, V)
         dO = make_upstream_grad(w).to(dev)
         pipe.backward(dO)
+        if pipe.global_layout:
+            gbwd_evs = timed(lambda: cpa.share_backward(
+                Q, K, V, pos_d, pipe.O, dO, pipe.lse, w.N, w.causal, pipe.dK, pipe.dV,
+                pipe.scale, rank, rank + 1, dQ=pipe.dQ, delta=pipe.delta), reps)
+        zigzag(pipe.O, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=pipe.Or)
+        zigzag(pipe.lse, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=pipe.lser)
+        dOr = zigzag(dO, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1)
+        f32 = dict(dtype=torch.float32, device=dev)
+        dQr = torch.empty((w.B, w.H, Lr, w.D), **f32)
+        deltar = torch.empty((w.B, w.H, Lr), **f32)
+        dKr = torch.zeros(pipe.Kr.shape, **f32)
+        dVr = torch.zeros(pipe.Vr.shape, **f32)
         bwd_evs = timed(lambda: cpa.rank_backward(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr, pos_d,
-                                                  pipe.Or[0], pipe.dOr[0], pipe.lser[0],
-                                                  w.causal, pipe.dKr, pipe.dVr, pipe.scale,
-                                                  dQ=pipe.dQr[0], delta=pipe.deltar[0]), reps)
+                                                  pipe.Or[0], dOr[0], pipe.lser[0], w.causal,
+                                                  dKr, dVr, pipe.scale, dQ=dQr, delta=deltar),
+                        reps)
     torch.cuda.synchronize()
     p_ms = np.array([a.elapsed_time(b) for _, (a, b) in part_evs])
     p_flops = np.array([4.0 * w.D * w.B * w.H * pairs[j] for j, _ in part_evs])
@@ -278,12 +292,15 @@ def main():
     perm_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
     perm_bytes = 2 * K.numel() * K.element_size()
     rope_ms = float(np.mean([a.elapsed_time(b) for a, b in rope_evs]))
-    bwd = None
-    if bwd_evs:
-        b_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_evs]))
+    def bwd_report(evs):
+        if not evs:
+            return None
+        b_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         b_flop = 2.0 * useful  # dV, dP, dQ, dK: 4 products of 2*D per visible pair
-        bwd = {"ms": round(b_ms, 4), "TFLOP/s": round(b_flop / (b_ms * 1e-3) / 1e12, 2),
-               "useful_flop": b_flop}
+        return {"ms": round(b_ms, 4), "TFLOP/s": round(b_flop / (b_ms * 1e-3) / 1e12, 2),
+                "useful_flop": b_flop}
+    bwd = bwd_report(bwd_evs)
+    gbwd = bwd_report(gbwd_evs)
 
     value = useful / (ms_step * 1e-3) / 1e12
     out = {
@@ -329,6 +346,7 @@ def main():
             "ms_per_step_events": round(ms_step_ev, 4),
             "step_ms_stats": stats(step_ms),
             "rank_backward": bwd,
+            "share_backward": gbwd,
         },
         "cpu_baseline": None,
     }

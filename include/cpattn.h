@@ -247,6 +247,33 @@ cpa_status cpa_rank_backward(int32_t i, int32_t N, const void *Q_i, const void *
                              float *dQ_i, float *dK_all, float *dV_all, float *delta_i,
                              void *stream);
 
+/*
+ * The ranks' ring backward directly on global-order data: cpa_rank_backward
+ * for each rank r in [rank_lo, rank_hi), with the zigzag permute folded into
+ * the kernels' addressing as in cpa_share_forward (rank r's local row u is
+ * global row zig(r, u)), so no tensor is permuted before or after.
+ *   Q, K, V, dO   device [B, H, L, D] bf16, global order
+ *   O, lse        device float32 [B, H, L, D] / [B, H, L]: the forward's
+ *                 output in global order (cpa_share_forward)
+ *   pos_all       device int64 [N, L/N]: cpa_zigzag_layout(L, N)'s table
+ *   dQ            device float32 [B, H, L, D]: the selected ranks' rows are
+ *                 WRITTEN, the others are left untouched
+ *   dK, dV        device float32 [B, H, L, D]: the selected ranks'
+ *                 contributions are ADDED (zero them first; after all N ranks
+ *                 they hold the full dK, dV in global order)
+ *   delta         device float32 [B, H, L]: the selected ranks' rows are
+ *                 written (workspace, kept for reuse)
+ *   causal, scale as for cpa_partial
+ * bf16 with D = 64 or 128 and L/(2N) a multiple of 32 (CPA_EUNSUPPORTED
+ * otherwise; use the permute + cpa_rank_backward path).  Three launches per
+ * rank: delta, the dQ pass and the dK/dV pass.
+ */
+cpa_status cpa_share_backward(const void *Q, const void *K, const void *V, const int64_t *pos_all,
+                              const float *O, const void *dO, const float *lse, cpa_dtype dt,
+                              int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+                              int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
+                              float *dQ, float *dK, float *dV, float *delta, void *stream);
+
 /* Pairing of the elements a rotary embedding rotates together. */
 typedef enum {
   CPA_ROPE_INTERLEAVED = 0, /* pairs (2k, 2k+1), as the sinusoidal table interleaves sin/cos */

@@ -12,8 +12,8 @@ from ._lib import (CPA_BF16, CPA_F32, CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED,  # no
                    CpaError, check, last_error, load, version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
-           "rank_forward_fused", "share_forward", "zigzag_permute", "rope", "zigzag_permute_rope",
-           "backward_delta", "partial_backward", "rank_backward", "last_error",
+           "rank_forward_fused", "share_forward", "share_backward", "zigzag_permute", "rope",
+           "zigzag_permute_rope", "backward_delta", "partial_backward", "rank_backward", "last_error",
            "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
 
 
@@ -145,6 +145,28 @@ def share_forward(Q, K, V, pos_all, N: int, causal: bool, scale: float = 0.0, ra
                                    L, D, N, rank_lo, rank_hi, int(bool(causal)), float(scale),
                                    _ptr(out), _ptr(lse), _stream(Q)))
     return out, lse
+
+
+def share_backward(Q, K, V, pos_all, O, dO, lse, N: int, causal: bool, dK, dV,
+                   scale: float = 0.0, rank_lo: int = 0, rank_hi: int | None = None, dQ=None,
+                   delta=None):
+    """Ring backward of ranks [rank_lo, rank_hi) on global-order bf16 Q/K/V/dO
+    [B,H,L,D] with the forward's global-order O [B,H,L,D] and lse [B,H,L]
+    (float32): returns dQ (the selected ranks' rows written) and adds their
+    contributions into the global-order float32 accumulators dK, dV."""
+    torch = _torch()
+    rank_hi = N if rank_hi is None else rank_hi
+    B, H, L, D = Q.shape
+    if dQ is None:
+        dQ = torch.zeros((B, H, L, D), dtype=torch.float32, device=Q.device)
+    if delta is None:
+        delta = torch.empty((B, H, L), dtype=torch.float32, device=Q.device)
+    _need_gpu(Q, K, V, pos_all, O, dO, lse, dK, dV, dQ, delta)
+    check(load().cpa_share_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _ptr(O), _ptr(dO),
+                                    _ptr(lse), _dtype_code(Q), B, H, L, D, N, rank_lo, rank_hi,
+                                    int(bool(causal)), float(scale), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                    _ptr(delta), _stream(Q)))
+    return dQ
 
 
 def zigzag_permute(src, pos_all, N: int, inverse: bool = False, rank_lo: int = 0,

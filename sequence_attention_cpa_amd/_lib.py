@@ -44,6 +44,9 @@ SIGNATURES = {
     "cpa_rank_backward": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          ctypes.c_int, _i32, _i32, _i64, _i32, _i32, _f32, _vp, _vp,
                                          _vp, _vp, _vp]),
+    "cpa_share_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+                                          _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                          _vp, _vp, _vp, _vp]),
     "cpa_rope": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32, _vp, _f64, _i32,
                                 _vp]),
     "cpa_zigzag_permute_rope": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32, _vp,

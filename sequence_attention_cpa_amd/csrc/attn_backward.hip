@@ -161,9 +161,20 @@ __device__ __forceinline__ float lse_ref(float l) {
   return l == -INFINITY ? INFINITY : l * LOG2E;
 }
 
+// Rows of the global-order (zigzag) layout: rank r's local row u of Lr rows
+// is global row r*C + u for u < C and (2N-1-r)*C + (u - C) after, C = Lr/2.
+// With C a multiple of 32, every 32-row tile is contiguous in global order.
+__device__ __forceinline__ int64_t zig_row(int r, int64_t u, int64_t Lr, int nblk) {
+  const int64_t C = Lr / 2;
+  return u < C ? (int64_t)r * C + u : (int64_t)(2 * nblk - 1 - r) * C + (u - C);
+}
+
 // ---------------------------------------------------------------- dQ pass
 
-template <int D>
+// GL: Q, K, V, dO, lse, delta and dQ are the whole sequence in global token
+// order ([BH, nblk * Lq, ...]); the queries are rank `first`'s rows and K/V
+// block b is rank b's rows, all through zig_row.
+template <int D, bool GL>
 __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -195,14 +206,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   const int64_t q_first = causal ? q_off[q_base] : 0;
   const int64_t q_last = causal ? q_off[last_row] : 0;
   const int64_t my_qpos = causal ? q_off[qrow_c] : 0;
-  const float l2 = lse_ref(lse[(int64_t)bh * Lq + qrow_c]);
-  const float dl = delta[(int64_t)bh * Lq + qrow_c];
+  const int64_t Lrow = GL ? Lq * nblk : Lq;  // rows per head of Q, dO, lse, delta, dQ
+  auto qmap = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
+    return GL ? zig_row(first, u, Lq, nblk) : u;
+  };
+  const int64_t qg = (int64_t)bh * Lrow + qmap(qrow_c);
+  const float l2 = lse_ref(lse[qg]);
+  const float dl = delta[qg];
 
   // Q and dO rows of this wave as B operands (lane: 8 columns of its query).
   bf16x8 qf[KK], df[KK];
   {
-    const __bf16* qr = Q + ((int64_t)bh * Lq + qrow_c) * D;
-    const __bf16* dr = dO + ((int64_t)bh * Lq + qrow_c) * D;
+    const __bf16* qr = Q + qg * D;
+    const __bf16* dr = dO + qg * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       qf[kk] = *reinterpret_cast<const bf16x8*>(qr + kk * 16 + hi * 8);
@@ -223,16 +239,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   const f32x16 zero16 = {};
 
-  const __bf16* Kbh = nullptr;
-  const __bf16* Vbh = nullptr;
+  // Current block: K / V bases.  GL: a block's keys below C come from its
+  // first chunk (base *_lo), the rest from its second (base *_hi, offset by
+  // -C rows so that key u sits at base + u * D in both).
+  const __bf16 *Kbh = nullptr, *Vbh = nullptr, *Kbh_hi = nullptr, *Vbh_hi = nullptr;
+  const int64_t C = Lq / 2;
   int64_t n_lo = Lk, n_hi = Lk, my_n = Lk;
   int T = 0;
+  // Tile t (keys [t*BN, t*BN + BN)) of the current block's K or V into LDS.
+  auto copy_kv = [&](const __bf16* lo, const __bf16* hi_base, int t, lds_char* dst)
+                     __attribute__((always_inline)) {
+    const int64_t u0 = (int64_t)t * BN;
+    ta.copy((GL && u0 >= C) ? hi_base : lo, u0, Lk, dst);
+  };
 
   auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
     constexpr int P = decltype(P_)::value;
     if (t + 1 < T) {
-      ta.copy(Kbh, (int64_t)(t + 1) * BN, Lk, Kl + (P ^ 1) * TB);
-      ta.copy(Vbh, (int64_t)(t + 1) * BN, Lk, Vl + (P ^ 1) * TB);
+      copy_kv(Kbh, Kbh_hi, t + 1, Kl + (P ^ 1) * TB);
+      copy_kv(Vbh, Vbh_hi, t + 1, Vl + (P ^ 1) * TB);
     }
     const lds_char* Kt = Kl + P * TB;
     const lds_char* Vt = Vl + P * TB;
@@ -276,8 +301,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
 
   for (int sb = 0; sb < nblk; ++sb) {
     const int blk = (first + 1 + sb) % nblk;
-    Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
-    Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
+    if constexpr (GL) {
+      const int64_t lo_row = (int64_t)blk * C, hi_row = (int64_t)(2 * nblk - 1 - blk) * C - C;
+      Kbh = K + ((int64_t)bh * Lrow + lo_row) * D;
+      Vbh = V + ((int64_t)bh * Lrow + lo_row) * D;
+      Kbh_hi = K + ((int64_t)bh * Lrow + hi_row) * D;
+      Vbh_hi = V + ((int64_t)bh * Lrow + hi_row) * D;
+    } else {
+      Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
+      Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
+      Kbh_hi = Kbh;
+      Vbh_hi = Vbh;
+    }
     if (causal) {
       const int64_t* kb_off = k_off + blk * koff_stride;
       n_lo = count_le(kb_off, Lk, q_first);
@@ -291,8 +326,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     }
     if (n_hi == 0) continue;
     T = (int)((n_hi + BN - 1) / BN);
-    ta.copy(Kbh, 0, Lk, Kl);
-    ta.copy(Vbh, 0, Lk, Vl);
+    copy_kv(Kbh, Kbh_hi, 0, Kl);
+    copy_kv(Vbh, Vbh_hi, 0, Vl);
     wait_copies();
     __syncthreads();
     int t = 0;
@@ -304,7 +339,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   }
 
   if (qrow < Lq) {
-    float* orow = dQ + ((int64_t)bh * Lq + qrow) * D;
+    float* orow = dQ + ((int64_t)bh * Lrow + qmap(qrow)) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -331,13 +366,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
 // dK^T += Q^T dS.  A barrier in the middle of each tile publishes P.  Each
 // wave keeps one 32 x D accumulator and one of K / V, so two waves fit per
 // SIMD, and no product is computed twice.
-template <int D>
+// GL: all tensors in global token order ([BH, nblk * Lq, ...]); the queries
+// are rank `qrank`'s rows and K/V block b (with its dK/dV rows) is rank b's,
+// all through zig_row.
+template <int D, bool GL>
 __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ dK,
     float* __restrict__ dV, int BH, int64_t Lq, int64_t Lk, int64_t kv_stride,
-    int64_t koff_stride, int causal, float scale, int n_ktiles) {
+    int64_t koff_stride, int causal, float scale, int n_ktiles, int nblk, int qrank) {
   using G = Geo<D>;
   constexpr int TB = G::TILE_BYTES;
   constexpr int KK = G::KK;
@@ -367,12 +405,27 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   const int64_t krow_c = krow < Lk ? krow : Lk - 1;
   const float c_log2 = scale * LOG2E;
 
-  const __bf16* Kb = K + blk * kv_stride + (int64_t)bh * Lk * D;
-  const __bf16* Vb = V + blk * kv_stride + (int64_t)bh * Lk * D;
-  const __bf16* Qbh = Q + (int64_t)bh * Lq * D;
-  const __bf16* Obh = dO + (int64_t)bh * Lq * D;
-  const float* lse_bh = lse + (int64_t)bh * Lq;
-  const float* dl_bh = delta + (int64_t)bh * Lq;
+  const int64_t Lrow = GL ? Lq * nblk : Lq;  // rows per head of every tensor (GL)
+  // Row of key u of this block / of query u of the rank, within a head.
+  auto kmap = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
+    return GL ? zig_row(blk, u, Lk, nblk) : u;
+  };
+  auto qmap = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
+    return GL ? zig_row(qrank, u, Lq, nblk) : u;
+  };
+  const __bf16* Kb = GL ? K + (int64_t)bh * Lrow * D : K + blk * kv_stride + (int64_t)bh * Lk * D;
+  const __bf16* Vb = GL ? V + (int64_t)bh * Lrow * D : V + blk * kv_stride + (int64_t)bh * Lk * D;
+  // The rank's Q / dO rows: GL, query u < C at Qbh + u * D (first chunk),
+  // u >= C at Qbh_hi + u * D (second chunk, base offset by -C rows).
+  const int64_t Cq = Lq / 2;
+  const int64_t q_lo_row = GL ? (int64_t)qrank * Cq : 0;
+  const int64_t q_hi_row = GL ? (int64_t)(2 * nblk - 1 - qrank) * Cq - Cq : 0;
+  const __bf16* Qbh = Q + ((int64_t)bh * Lrow + q_lo_row) * D;
+  const __bf16* Obh = dO + ((int64_t)bh * Lrow + q_lo_row) * D;
+  const __bf16* Qbh_hi = Q + ((int64_t)bh * Lrow + q_hi_row) * D;
+  const __bf16* Obh_hi = dO + ((int64_t)bh * Lrow + q_hi_row) * D;
+  const float* lse_bh = lse + (int64_t)bh * Lrow;
+  const float* dl_bh = delta + (int64_t)bh * Lrow;
 
   // Visible queries of a key form a suffix [first(u), Lq) of the query block:
   // m_lo / m_hi bound it for the workgroup's first / last key, my_first is
@@ -395,14 +448,20 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   const int T = (int)((Lq + BN - 1) / BN);
 
   const TileAddr<D, 8> ta(wv, lane);
+  // Query tile t (rows [t*BN, t*BN + BN)) of Q or dO into LDS.
+  auto copy_q = [&](const __bf16* lo, const __bf16* hi_base, int t, lds_char* dst)
+                    __attribute__((always_inline)) {
+    const int64_t u0 = (int64_t)t * BN;
+    ta.copy((GL && u0 >= Cq) ? hi_base : lo, u0, Lq, dst);
+  };
   const f32x16 zero16 = {};
 
   // lse reference and delta of query tile t into LDS buffer b (first wave).
   auto stage_rows = [&](int t, int b) __attribute__((always_inline)) {
     if (tid < BN) {
       const int64_t q = (int64_t)t * BN + tid;
-      l2_lds[b][tid] = q < Lq ? lse_ref(lse_bh[q]) : INFINITY;
-      dl_lds[b][tid] = q < Lq ? dl_bh[q] : 0.f;
+      l2_lds[b][tid] = q < Lq ? lse_ref(lse_bh[qmap(q)]) : INFINITY;
+      dl_lds[b][tid] = q < Lq ? dl_bh[qmap(q)] : 0.f;
     }
   };
 
@@ -413,7 +472,7 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
     // This lane's key row of K (P role) or V (dS role) as the B operand.
     bf16x8 rf[KK];
     {
-      const __bf16* src = (DKR ? Vb : Kb) + krow_c * D;
+      const __bf16* src = (DKR ? Vb : Kb) + kmap(krow_c) * D;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         rf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16 + hi * 8);
@@ -430,8 +489,8 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
     auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
       constexpr int P = decltype(P_)::value;
       if (t + 1 < T) {
-        ta.copy(Qbh, (int64_t)(t + 1) * BN, Lq, Ql + (P ^ 1) * TB);
-        ta.copy(Obh, (int64_t)(t + 1) * BN, Lq, Ol + (P ^ 1) * TB);
+        copy_q(Qbh, Qbh_hi, t + 1, Ql + (P ^ 1) * TB);
+        copy_q(Obh, Obh_hi, t + 1, Ol + (P ^ 1) * TB);
       }
       const lds_char* Qt = Ql + P * TB;
       const lds_char* Ot = Ol + P * TB;
@@ -498,8 +557,8 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
       __syncthreads();
     };
 
-    ta.copy(Qbh, (int64_t)t0 * BN, Lq, Ql);
-    ta.copy(Obh, (int64_t)t0 * BN, Lq, Ol);
+    copy_q(Qbh, Qbh_hi, t0, Ql);
+    copy_q(Obh, Obh_hi, t0, Ol);
     stage_rows(t0, 0);
     wait_copies();
     __syncthreads();
@@ -511,7 +570,9 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
     if (t < T) iter(t, I0{});
 
     if (krow < Lk) {
-      float* dst = (DKR ? dK : dV) + blk * kv_stride + ((int64_t)bh * Lk + krow) * D;
+      float* dst = (DKR ? dK : dV) +
+                   (GL ? ((int64_t)bh * Lrow + kmap(krow)) * D
+                       : blk * kv_stride + ((int64_t)bh * Lk + krow) * D);
       const float f = DKR ? scale : 1.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -554,26 +615,31 @@ __device__ __forceinline__ void load8f<float>(const float* p, float (&v)[8]) {
 
 // delta[row] = sum_d dO[row, d] * O[row, d]; GS = D/8 lanes per row, each
 // summing 8 products, then a butterfly over the GS lanes (GS divides 64).
-template <typename T, int GS>
+// GL: the rows are rank `rank`'s share of global-order [rows / Lr heads, nblk
+// * Lr, D] tensors: logical row (h, u) is physical row h * nblk * Lr + zig_row(rank, u).
+template <typename T, int GS, bool GL>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const float* __restrict__ O,
                                                         const T* __restrict__ dO,
-                                                        float* __restrict__ delta, int64_t rows) {
+                                                        float* __restrict__ delta, int64_t rows,
+                                                        int64_t Lr, int nblk, int rank) {
   constexpr int D = GS * 8;
   const int64_t per_block = 256 / GS;
   for (int64_t r0 = (int64_t)blockIdx.x * per_block; r0 < rows; r0 += (int64_t)gridDim.x * per_block) {
     const int64_t row = r0 + threadIdx.x / GS;
     const int part = threadIdx.x % GS;
+    const int64_t prow =
+        GL ? (row / Lr) * (Lr * nblk) + zig_row(rank, row % Lr, Lr, nblk) : row;
     float sum = 0.f;
     if (row < rows) {
       float o[8], g[8];
-      load8f<float>(O + row * D + part * 8, o);
-      load8f<T>(dO + row * D + part * 8, g);
+      load8f<float>(O + prow * D + part * 8, o);
+      load8f<T>(dO + prow * D + part * 8, g);
 #pragma unroll
       for (int i = 0; i < 8; ++i) sum = fmaf(o[i], g[i], sum);
     }
 #pragma unroll
     for (int m = GS / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, GS);
-    if (row < rows && part == 0) delta[row] = sum;
+    if (row < rows && part == 0) delta[prow] = sum;
   }
 }
 
@@ -692,23 +758,23 @@ unsigned grid_cap(int64_t blocks) {
   return (unsigned)blocks;
 }
 
-template <typename T>
+template <typename T, bool GL>
 hipError_t delta_dispatch(const float* O, const void* dO, int64_t rows, int D, float* delta,
-                          hipStream_t st) {
+                          int64_t Lr, int nblk, int rank, hipStream_t st) {
   const int GS = D / 8;
   const unsigned grid = grid_cap((rows * GS + 255) / 256);
   switch (GS) {
     case 2:
-      hipLaunchKernelGGL((bwd_delta_kernel<T, 2>), dim3(grid), dim3(256), 0, st, O, (const T*)dO,
-                         delta, rows);
+      hipLaunchKernelGGL((bwd_delta_kernel<T, 2, GL>), dim3(grid), dim3(256), 0, st, O,
+                         (const T*)dO, delta, rows, Lr, nblk, rank);
       break;
     case 8:
-      hipLaunchKernelGGL((bwd_delta_kernel<T, 8>), dim3(grid), dim3(256), 0, st, O, (const T*)dO,
-                         delta, rows);
+      hipLaunchKernelGGL((bwd_delta_kernel<T, 8, GL>), dim3(grid), dim3(256), 0, st, O,
+                         (const T*)dO, delta, rows, Lr, nblk, rank);
       break;
     default:
-      hipLaunchKernelGGL((bwd_delta_kernel<T, 16>), dim3(grid), dim3(256), 0, st, O,
-                         (const T*)dO, delta, rows);
+      hipLaunchKernelGGL((bwd_delta_kernel<T, 16, GL>), dim3(grid), dim3(256), 0, st, O,
+                         (const T*)dO, delta, rows, Lr, nblk, rank);
       break;
   }
   return hipGetLastError();
@@ -736,7 +802,7 @@ hipError_t rowwise_bwd(const void* Q, const void* K, const void* V, const void* 
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool GL>
 hipError_t mfma_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lse,
                     const float* delta, const int64_t* q_off, const int64_t* k_off, float* dQ,
                     float* dK, float* dV, int BH, int64_t Lq, int64_t Lk, int64_t kv_stride,
@@ -744,16 +810,17 @@ hipError_t mfma_bwd(const void* Q, const void* K, const void* V, const void* dO,
                     bool acc_dq, hipStream_t st) {
   const int n_qtiles = (int)((Lq + BM - 1) / BM);
   const int n_ktiles = (int)((Lk + BM - 1) / BM);
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(n_qtiles * BH)), dim3(NTHREADS), 0, st,
-                     (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, (const __bf16*)dO, lse,
-                     delta, q_off, k_off, dQ, BH, Lq, Lk, kv_stride, koff_stride, nblk, first,
-                     causal ? 1 : 0, scale, n_qtiles, acc_dq ? 1 : 0);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, GL>), dim3((unsigned)(n_qtiles * BH)), dim3(NTHREADS), 0,
+                     st, (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, (const __bf16*)dO,
+                     lse, delta, q_off, k_off, dQ, BH, Lq, Lk, kv_stride, koff_stride, nblk,
+                     first, causal ? 1 : 0, scale, n_qtiles, acc_dq ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(nblk * n_ktiles * BH)), dim3(2 * NTHREADS),
-                     0, st, (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V,
-                     (const __bf16*)dO, lse, delta, q_off, k_off, dK, dV, BH, Lq, Lk, kv_stride,
-                     koff_stride, causal ? 1 : 0, scale, n_ktiles);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, GL>), dim3((unsigned)(nblk * n_ktiles * BH)),
+                     dim3(2 * NTHREADS), 0, st, (const __bf16*)Q, (const __bf16*)K,
+                     (const __bf16*)V, (const __bf16*)dO, lse, delta, q_off, k_off, dK, dV, BH,
+                     Lq, Lk, kv_stride, koff_stride, causal ? 1 : 0, scale, n_ktiles, nblk,
+                     first);
   return hipGetLastError();
 }
 
@@ -762,8 +829,15 @@ hipError_t mfma_bwd(const void* Q, const void* K, const void* V, const void* dO,
 hipError_t launch_bwd_delta(const float* O, const void* dO, bool bf16, int64_t rows, int D,
                             float* delta, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  return bf16 ? delta_dispatch<__bf16>(O, dO, rows, D, delta, stream)
-              : delta_dispatch<float>(O, dO, rows, D, delta, stream);
+  return bf16 ? delta_dispatch<__bf16, false>(O, dO, rows, D, delta, 1, 1, 0, stream)
+              : delta_dispatch<float, false>(O, dO, rows, D, delta, 1, 1, 0, stream);
+}
+
+hipError_t launch_bwd_delta_share(const float* O, const void* dO, int BH, int64_t Lr, int N,
+                                  int i, int D, float* delta, hipStream_t stream) {
+  const int64_t rows = (int64_t)BH * Lr;
+  if (rows == 0) return hipSuccess;
+  return delta_dispatch<__bf16, true>(O, dO, rows, D, delta, Lr, N, i, stream);
 }
 
 hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const void* dO,
@@ -773,10 +847,22 @@ hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const vo
                            int nblk, int first, int D, bool causal, float scale, bool acc_dq,
                            hipStream_t stream) {
   if (D == 128)
-    return mfma_bwd<128>(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV, BH, Lq, Lk,
-                         kv_stride, koff_stride, nblk, first, causal, scale, acc_dq, stream);
-  return mfma_bwd<64>(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV, BH, Lq, Lk, kv_stride,
-                      koff_stride, nblk, first, causal, scale, acc_dq, stream);
+    return mfma_bwd<128, false>(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV, BH, Lq, Lk,
+                                kv_stride, koff_stride, nblk, first, causal, scale, acc_dq,
+                                stream);
+  return mfma_bwd<64, false>(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV, BH, Lq, Lk,
+                             kv_stride, koff_stride, nblk, first, causal, scale, acc_dq, stream);
+}
+
+hipError_t launch_bwd_share_mfma(const void* Q, const void* K, const void* V, const void* dO,
+                                 const float* lse, const float* delta, const int64_t* pos_all,
+                                 float* dQ, float* dK, float* dV, int BH, int64_t Lr, int N, int i,
+                                 int D, bool causal, float scale, hipStream_t stream) {
+  if (D == 128)
+    return mfma_bwd<128, true>(Q, K, V, dO, lse, delta, pos_all + (int64_t)i * Lr, pos_all, dQ,
+                               dK, dV, BH, Lr, Lr, 0, Lr, N, i, causal, scale, false, stream);
+  return mfma_bwd<64, true>(Q, K, V, dO, lse, delta, pos_all + (int64_t)i * Lr, pos_all, dQ, dK,
+                            dV, BH, Lr, Lr, 0, Lr, N, i, causal, scale, false, stream);
 }
 
 hipError_t launch_bwd_rowwise(const void* Q, const void* K, const void* V, const void* dO,

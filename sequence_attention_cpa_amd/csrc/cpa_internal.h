@@ -69,6 +69,17 @@ hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const vo
                            int nblk, int first, int D, bool causal, float scale, bool acc_dq,
                            hipStream_t stream);
 
+// Backward of ranks' shares on global-order data (bf16, D = 64 or 128, Lr/2
+// % 32 == 0): tensors are [BH, N*Lr, ...] in global token order and rank r's
+// local row u is global row zig(r, u).  delta of rank i's rows; then rank
+// i's dQ (written) and its contributions to every block's dK / dV (added).
+hipError_t launch_bwd_delta_share(const float* O, const void* dO, int BH, int64_t Lr, int N,
+                                  int i, int D, float* delta, hipStream_t stream);
+hipError_t launch_bwd_share_mfma(const void* Q, const void* K, const void* V, const void* dO,
+                                 const float* lse, const float* delta, const int64_t* pos_all,
+                                 float* dQ, float* dK, float* dV, int BH, int64_t Lr, int N, int i,
+                                 int D, bool causal, float scale, hipStream_t stream);
+
 // Backward of one block, one row per thread in fp32 (fp32 inputs; bf16 with D = 16).
 hipError_t launch_bwd_rowwise(const void* Q, const void* K, const void* V, const void* dO,
                               bool bf16, const float* lse, const float* delta,

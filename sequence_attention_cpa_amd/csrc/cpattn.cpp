@@ -396,4 +396,43 @@ cpa_status cpa_rank_backward(int32_t i, int32_t N, const void* Q_i, const void* 
   return ok();
 }
 
+cpa_status cpa_share_backward(const void* Q, const void* K, const void* V, const int64_t* pos_all,
+                              const float* O, const void* dO, const float* lse, cpa_dtype dt,
+                              int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+                              int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
+                              float* dQ, float* dK, float* dV, float* delta, void* stream) {
+  if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (rank_lo < 0 || rank_hi > N || rank_lo >= rank_hi)
+    return fail(CPA_EINVAL, "rank range [%d, %d) invalid for N=%d", rank_lo, rank_hi, N);
+  const int64_t Lr = L / N;
+  if (dt != CPA_BF16 || (D != 64 && D != 128))
+    return fail(CPA_EUNSUPPORTED, "the global-layout backward runs bf16 with D = 64 or 128");
+  if ((Lr / 2) % 32 != 0)
+    return fail(CPA_EUNSUPPORTED, "the global-layout backward needs chunks L/(2N) that are "
+                                  "multiples of 32 (L=%lld, N=%d); use the rank-major path",
+                (long long)L, N);
+  if (Lr > ((int64_t)1 << 30)) return fail(CPA_ESHAPE, "L/N is limited to 2^30 rows");
+  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if (!Q || !K || !V || !pos_all || !O || !dO || !lse || !dQ || !dK || !dV || !delta)
+    return fail(CPA_EINVAL, "null pointer");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(dO, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
+    return fail(CPA_EINVAL, "Q, K, V, O, dO, dQ, dK and dV must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(delta, 4) || !aligned(pos_all, 8))
+    return fail(CPA_EINVAL, "lse and delta must be 4-byte and pos_all 8-byte aligned");
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
+  const int BH = B * H;
+  hipStream_t s = (hipStream_t)stream;
+  for (int32_t r = rank_lo; r < rank_hi; ++r) {
+    hipError_t e = cpa::launch_bwd_delta_share(O, dO, BH, Lr, N, r, D, delta, s);
+    if (e != hipSuccess) return from_hip(e, "backward delta launch");
+    e = cpa::launch_bwd_share_mfma(Q, K, V, dO, lse, delta, pos_all, dQ, dK, dV, BH, Lr, N, r, D,
+                                   causal != 0, scale, s);
+    if (e != hipSuccess) return from_hip(e, "global-layout ring backward launch");
+  }
+  return ok();
+}
+
 }  // extern "C"

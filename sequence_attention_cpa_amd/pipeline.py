@@ -23,8 +23,10 @@ folded into the permute, so it costs no extra pass over memory).
 `backward(dO)` runs the ring backward of the ranks after a `step`: dO is
 permuted like Q, each rank's cpa_rank_backward writes its dQ and adds its
 contributions to every block's dK / dV (rank-major float32 accumulators,
-cleared first), and the gradients are scattered back to global order.  With
-RoPE the returned dQ, dK are gradients with respect to the rotated Q, K.
+cleared first), and the gradients are scattered back to global order.  In
+global-layout mode it is one cpa_share_backward call per rank on the
+global-order tensors instead (no permutes).  With RoPE the returned dQ, dK
+are gradients with respect to the rotated Q, K.
 
 All buffers are allocated once in the constructor (the backward's on first
 use); `step` and `backward` allocate nothing after that.
@@ -32,8 +34,8 @@ use); `step` and `backward` allocate nothing after that.
 from __future__ import annotations
 
 from . import (CPA_ROPE_INTERLEAVED, rank_backward, rank_forward, rank_forward_fused,
-               rank_forward_workspace, share_forward, zigzag_layout, zigzag_permute,
-               zigzag_permute_rope)
+               rank_forward_workspace, share_backward, share_forward, zigzag_layout,
+               zigzag_permute, zigzag_permute_rope)
 
 
 class SharePipeline:
@@ -104,23 +106,26 @@ class SharePipeline:
         import torch
 
         N, lo, hi = self.N, self.rank_lo, self.rank_hi
+        f32 = dict(dtype=torch.float32, device=self.Kr.device)
+        if not hasattr(self, "dQ"):
+            self.dQ = torch.zeros((self.B, self.H, self.L, self.D), **f32)
+            self.dK = torch.empty_like(self.dQ)
+            self.dV = torch.empty_like(self.dQ)
+        if self.global_layout:
+            if not hasattr(self, "delta"):
+                self.delta = torch.zeros((self.B, self.H, self.L), **f32)
+            Q, K, V = self._inputs
+            self.dK.zero_()
+            self.dV.zero_()
+            share_backward(Q, K, V, self.pos, self.O, dO, self.lse, N, self.causal, self.dK,
+                           self.dV, self.scale, lo, hi, dQ=self.dQ, delta=self.delta)
+            return self.dQ, self.dK, self.dV
         if not hasattr(self, "dOr"):
-            f32 = dict(dtype=torch.float32, device=self.Kr.device)
             self.dOr = torch.empty_like(self.Qr)
             self.dQr = torch.empty(self.Qr.shape, **f32)
             self.deltar = torch.empty(self.lser.shape, **f32)
             self.dKr = torch.empty(self.Kr.shape, **f32)
             self.dVr = torch.empty(self.Vr.shape, **f32)
-            self.dQ = torch.zeros((self.B, self.H, self.L, self.D), **f32)
-            self.dK = torch.empty_like(self.dQ)
-            self.dV = torch.empty_like(self.dQ)
-        if self.global_layout:  # the ring backward works on rank-major data
-            Q, K, V = self._inputs
-            zigzag_permute(K, self.pos, N, out=self.Kr)
-            zigzag_permute(V, self.pos, N, out=self.Vr)
-            zigzag_permute(Q, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Qr)
-            zigzag_permute(self.O, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.Or)
-            zigzag_permute(self.lse, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.lser)
         zigzag_permute(dO, self.pos, N, rank_lo=lo, rank_hi=hi, out=self.dOr)
         self.dKr.zero_()
         self.dVr.zero_()

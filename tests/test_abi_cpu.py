@@ -375,3 +375,33 @@ def _share(lib, **kw):
 def test_share_forward_rejects(lib, kw, status):
     assert _share(lib, **kw) == status
     assert cpa.last_error() != ""
+
+
+def _share_bwd(lib, **kw):
+    a = dict(Q=P, K=P, V=P, pos=P, O=P, dO=P, lse=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128,
+             N=4, lo=0, hi=4, causal=1, scale=0.0, dQ=P, dK=P, dV=P, delta=P, stream=None)
+    a.update(kw)
+    return lib.cpa_share_backward(a["Q"], a["K"], a["V"], a["pos"], a["O"], a["dO"], a["lse"],
+                                  a["dt"], a["B"], a["H"], a["L"], a["D"], a["N"], a["lo"],
+                                  a["hi"], a["causal"], a["scale"], a["dQ"], a["dK"], a["dV"],
+                                  a["delta"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=500), _lib.CPA_ESHAPE),
+    (dict(L=128), _lib.CPA_EUNSUPPORTED),      # chunks of 16 rows: not a multiple of 32
+    (dict(L=1000), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=_lib.CPA_F32), _lib.CPA_EUNSUPPORTED),
+    (dict(D=16), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=6), _lib.CPA_EDTYPE),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(lo=3, hi=3), _lib.CPA_EINVAL),
+    (dict(hi=5), _lib.CPA_EINVAL),
+    (dict(delta=None), _lib.CPA_EINVAL),
+    (dict(O=None), _lib.CPA_EINVAL),
+    (dict(dK=P + 4), _lib.CPA_EINVAL),
+    (dict(lse=P + 2), _lib.CPA_EINVAL),
+])
+def test_share_backward_rejects(lib, kw, status):
+    assert _share_bwd(lib, **kw) == status
+    assert cpa.last_error() != ""

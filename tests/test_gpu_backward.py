@@ -122,7 +122,11 @@ RANK_BWD_CASES = [
     (torch.bfloat16, 1, 2, 1536, 4, 128, False, True),
     (torch.bfloat16, 1, 2, 2048, 1, 128, True, True),
     (torch.bfloat16, 1, 2, 256, 16, 128, True, True),   # chunks of 8: every tile masked
-    (torch.bfloat16, 2, 2, 2048, 4, 128, True, "global"),  # forward step on global layout
+    (torch.bfloat16, 2, 2, 2048, 4, 128, True, "global"),  # both passes on global layout
+    (torch.bfloat16, 1, 3, 4096, 8, 128, True, "global"),
+    (torch.bfloat16, 2, 2, 1024, 4, 64, True, "global"),
+    (torch.bfloat16, 1, 2, 1536, 4, 128, False, "global"),  # chunks of 192 rows
+    (torch.bfloat16, 1, 2, 2048, 1, 128, True, "global"),
     (torch.bfloat16, 1, 2, 1000, 4, 128, True, True),   # 250 rows per rank: ragged tiles
     (torch.bfloat16, 2, 3, 1000, 4, 64, True, True),
     (torch.float32, 1, 2, 64, 4, 16, True, False),      # the fp32 tiny shape
@@ -158,23 +162,26 @@ def oracle_backward_heads(Q, K, V, dO, heads, causal=True):
 
 def test_ring_backward_12k_eight_heads_every_row():
     """The 12k workload's shape (L = 12288, N = 4, D = 128) on its first 8
-    heads, every gradient entry."""
+    heads, every gradient entry, on rank-major and on global-order data."""
     w = WORKLOADS["12k"]
     Q, K, V, _ = make_inputs(w)
     dO = make_upstream_grad(w)
     Q, K, V, dO = (x[:, :8].contiguous() for x in (Q, K, V, dO))
     say("12k bwd: GPU")
-    got = run_pipeline(Q, K, V, dO, w.N, w.causal, True)
+    got = {mode: run_pipeline(Q, K, V, dO, w.N, w.causal, mode) for mode in (True, "global")}
     say("12k bwd: oracle")
     ref = oracle_backward_heads(Q, K, V, dO, [(0, h) for h in range(8)])
-    for n, name in enumerate(("dQ", "dK", "dV")):
-        r = np.stack([ref[(0, h)][n] for h in range(8)])[None]
-        e = assert_grad_close(got[n], r, True, f"12k {name}")
-        say(f"12k bwd {name}: {e[0]:.3e} {e[1]:.3e}")
+    for mode, g in got.items():
+        for n, name in enumerate(("dQ", "dK", "dV")):
+            r = np.stack([ref[(0, h)][n] for h in range(8)])[None]
+            e = assert_grad_close(g[n], r, True, f"12k {mode} {name}")
+            say(f"12k bwd {mode} {name}: {e[0]:.3e} {e[1]:.3e}")
 
 
-def test_ring_backward_128k_sampled():
-    """128k workload, all 4 ranks (fused forward, ring backward).  dQ at the
+@pytest.mark.parametrize("mode", [True, "global"])
+def test_ring_backward_128k_sampled(mode):
+    """128k workload, all 4 ranks (forward, ring backward; rank-major or on
+    global-order data).  dQ at the
     sampled query rows of rank 0 and rank 3; dK, dV at every key of the last
     512 positions (all queries that see them are in the last 512 rows, so the
     oracle needs only those rows); and two sums that hold at any size: dK sums
@@ -183,7 +190,8 @@ def test_ring_backward_128k_sampled():
     say("128k bwd: generating")
     Q, K, V, outl = make_inputs(w)
     dO = make_upstream_grad(w)
-    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=True)
+    pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=True,
+                         global_layout=mode == "global")
     pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     dQ, dK, dV = pipe.backward(dO.to(DEV))
     torch.cuda.synchronize()
@@ -212,8 +220,8 @@ def test_ring_backward_128k_sampled():
     res = dict((h, (a, b, c)) for h, a, b, c in host_map(one, range(w.H)))
     for n, (name, got) in enumerate((("dQ", dQs), ("dK", dKs), ("dV", dVs))):
         r = np.stack([res[h][n] for h in range(w.H)])[None]
-        e = assert_grad_close(got, r, True, f"128k {name}")
-        say(f"128k bwd {name}: {e[0]:.3e} {e[1]:.3e}")
+        e = assert_grad_close(got, r, True, f"128k {mode} {name}")
+        say(f"128k bwd {mode} {name}: {e[0]:.3e} {e[1]:.3e}")
     sum_dO = dO.double().sum(dim=2).numpy()
     assert np.all(np.abs(sum_dK) <= 1e-3 * abs_dK), float(np.max(np.abs(sum_dK) / abs_dK))
     assert np.all(np.abs(sum_dV - sum_dO) <= 1e-3 * dO.double().abs().sum(dim=2).numpy())
@@ -237,3 +245,40 @@ def test_partial_backward_explicit_scale():
     torch.cuda.synchronize()
     for name, a, r in zip(("dQ", "dK", "dV"), acc, ref):
         assert_grad_close(a.cpu().double().numpy(), r, True, f"scale {name}")
+
+
+def test_share_backward_rank_subset():
+    """cpa_share_backward for ranks [1, 3) only: their dQ rows equal the
+    oracle's per-rank ring backward, the other ranks' dQ rows stay untouched,
+    and dK / dV hold exactly the two ranks' contributions, in global order."""
+    B, H, L, N, D, causal = 1, 2, 2048, 4, 128, True
+    Q, K, V, dO = (rand((B, H, L, D), torch.bfloat16, 300 + i) for i in range(4))
+    pos = cpa.zigzag_layout(L, N)
+    posd = pos.to(DEV)
+    Qd, Kd, Vd, dOd = (x.to(DEV) for x in (Q, K, V, dO))
+    O, lse = cpa.share_forward(Qd, Kd, Vd, posd, N, causal)
+    dK = torch.zeros((B, H, L, D), dtype=torch.float32, device=DEV)
+    dV = torch.zeros_like(dK)
+    dQ = torch.full((B, H, L, D), 7.0, dtype=torch.float32, device=DEV)
+    cpa.share_backward(Qd, Kd, Vd, posd, O, dOd, lse, N, causal, dK, dV, rank_lo=1, rank_hi=3,
+                       dQ=dQ)
+    torch.cuda.synchronize()
+    dQ, dK, dV = (x.cpu().double().numpy() for x in (dQ, dK, dV))
+    p = pos.numpy()
+    q64, k64, v64, g64 = (widen(x) for x in (Q, K, V, dO))
+    O64, lse64 = cpa_oracle.attention(q64, k64, v64, causal)
+    delta64 = cpa_oracle.backward_delta(O64, g64)
+    K_ranks = np.stack([k64[:, :, p[j]] for j in range(N)])
+    V_ranks = np.stack([v64[:, :, p[j]] for j in range(N)])
+    dK_ref, dV_ref = np.zeros_like(k64), np.zeros_like(v64)
+    for i in (1, 2):
+        dq, dk, dv = cpa_oracle.rank_backward(i, q64[:, :, p[i]], K_ranks, V_ranks,
+                                              g64[:, :, p[i]], lse64[:, :, p[i]],
+                                              delta64[:, :, p[i]], p, causal)
+        assert_grad_close(dQ[:, :, p[i]], dq, True, f"rank {i} dQ")
+        for j in range(N):
+            dK_ref[:, :, p[j]] += dk[j]
+            dV_ref[:, :, p[j]] += dv[j]
+    assert np.all(dQ[:, :, np.concatenate([p[0], p[3]])] == 7.0), "other ranks' dQ rows changed"
+    assert_grad_close(dK, dK_ref, True, "dK of ranks 1-2")
+    assert_grad_close(dV, dV_ref, True, "dV of ranks 1-2")
