@@ -8,8 +8,8 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (CPA_BF16, CPA_F32, CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED,  # noqa: F401
-                   CpaError, check, last_error, load, version)
+from ._lib import (CPA_BF16, CPA_EDTYPE, CPA_ESHAPE, CPA_F32, CPA_ROPE_HALF,  # noqa: F401
+                   CPA_ROPE_INTERLEAVED, CpaError, check, last_error, load, version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
            "rank_forward_fused", "share_forward", "share_backward", "zigzag_permute", "rope",
@@ -38,6 +38,17 @@ def _ptr(t):
 def _stream(t):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _expect(t, shape, dtypes, name):
+    """Reject a tensor whose shape or dtype disagrees with the sizes the C call
+    is given: the library sees raw pointers and would read or write past it."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise CpaError(CPA_ESHAPE, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise CpaError(CPA_EDTYPE, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
 
 
 def _need_gpu(*ts):
@@ -70,6 +81,13 @@ def partial(Q, K, V, q_off, k_off, causal: bool, scale: float = 0.0, out=None, l
         out = torch.empty((B, H, Lq, D), dtype=torch.float32, device=Q.device)
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=Q.device)
+    dt, f32, i64 = (Q.dtype,), (torch.float32,), (torch.int64,)
+    _expect(K, (B, H, Lk, D), dt, "K")
+    _expect(V, (B, H, Lk, D), dt, "V")
+    _expect(q_off, (Lq,), i64, "q_off")
+    _expect(k_off, (Lk,), i64, "k_off")
+    _expect(out, (B, H, Lq, D), f32, "out")
+    _expect(lse, (B, H, Lq), f32, "lse")
     _need_gpu(Q, K, V, q_off, k_off, out, lse)
     check(load().cpa_partial(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, Lq, Lk, D,
                              _ptr(q_off), _ptr(k_off), int(bool(causal)), float(scale),
@@ -79,6 +97,12 @@ def partial(Q, K, V, q_off, k_off, causal: bool, scale: float = 0.0, out=None, l
 
 def merge(O_acc, lse_acc, O_new, lse_new):
     """In-place online-softmax merge of (O_new, lse_new) into (O_acc, lse_acc)."""
+    torch = _torch()
+    f32 = (torch.float32,)
+    _expect(O_acc, O_acc.shape, f32, "O_acc")
+    _expect(O_new, O_acc.shape, f32, "O_new")
+    _expect(lse_acc, O_acc.shape[:-1], f32, "lse_acc")
+    _expect(lse_new, O_acc.shape[:-1], f32, "lse_new")
     _need_gpu(O_acc, lse_acc, O_new, lse_new)
     D = O_acc.shape[-1]
     rows = O_acc.numel() // D
@@ -89,6 +113,17 @@ def merge(O_acc, lse_acc, O_new, lse_new):
 
 def rank_forward_workspace(B: int, H: int, L: int, N: int, D: int) -> int:
     return int(load().cpa_rank_forward_workspace(B, H, L, N, D))
+
+
+def _check_rank_major(Q_i, K_all, V_all, pos_all, N, out, lse):
+    torch = _torch()
+    B, H, Lr, D = Q_i.shape
+    dt, f32 = (Q_i.dtype,), (torch.float32,)
+    _expect(K_all, (N, B, H, Lr, D), dt, "K_all")
+    _expect(V_all, (N, B, H, Lr, D), dt, "V_all")
+    _expect(pos_all, (N, Lr), (torch.int64,), "pos_all")
+    _expect(out, (B, H, Lr, D), f32, "out")
+    _expect(lse, (B, H, Lr), f32, "lse")
 
 
 def rank_forward(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool, scale: float = 0.0,
@@ -104,6 +139,9 @@ def rank_forward(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool, scale
     ws_bytes = rank_forward_workspace(B, H, L, N, D)
     if workspace is None and N > 1:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=Q_i.device)
+    _check_rank_major(Q_i, K_all, V_all, pos_all, N, out, lse)
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise CpaError(CPA_EDTYPE, f"workspace has dtype {workspace.dtype}, expected torch.uint8")
     _need_gpu(Q_i, K_all, V_all, pos_all, out, lse, workspace)
     check(load().cpa_rank_forward(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                   _dtype_code(Q_i), B, H, L, D, int(bool(causal)), float(scale),
@@ -121,6 +159,7 @@ def rank_forward_fused(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
         out = torch.empty((B, H, Lr, D), dtype=torch.float32, device=Q_i.device)
     if lse is None:
         lse = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
+    _check_rank_major(Q_i, K_all, V_all, pos_all, N, out, lse)
     _need_gpu(Q_i, K_all, V_all, pos_all, out, lse)
     check(load().cpa_rank_forward_fused(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                         _dtype_code(Q_i), B, H, Lr * N, D, int(bool(causal)),
@@ -140,6 +179,12 @@ def share_forward(Q, K, V, pos_all, N: int, causal: bool, scale: float = 0.0, ra
         out = torch.zeros((B, H, L, D), dtype=torch.float32, device=Q.device)
     if lse is None:
         lse = torch.full((B, H, L), float("-inf"), dtype=torch.float32, device=Q.device)
+    dt, f32 = (Q.dtype,), (torch.float32,)
+    _expect(K, (B, H, L, D), dt, "K")
+    _expect(V, (B, H, L, D), dt, "V")
+    _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
+    _expect(out, (B, H, L, D), f32, "out")
+    _expect(lse, (B, H, L), f32, "lse")
     _need_gpu(Q, K, V, pos_all, out, lse)
     check(load().cpa_share_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _dtype_code(Q), B, H,
                                    L, D, N, rank_lo, rank_hi, int(bool(causal)), float(scale),
@@ -161,6 +206,14 @@ def share_backward(Q, K, V, pos_all, O, dO, lse, N: int, causal: bool, dK, dV,
         dQ = torch.zeros((B, H, L, D), dtype=torch.float32, device=Q.device)
     if delta is None:
         delta = torch.empty((B, H, L), dtype=torch.float32, device=Q.device)
+    dt, f32 = (Q.dtype,), (torch.float32,)
+    for t, n in ((K, "K"), (V, "V"), (dO, "dO")):
+        _expect(t, (B, H, L, D), dt, n)
+    for t, n in ((O, "O"), (dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _expect(t, (B, H, L, D), f32, n)
+    _expect(lse, (B, H, L), f32, "lse")
+    _expect(delta, (B, H, L), f32, "delta")
+    _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _need_gpu(Q, K, V, pos_all, O, dO, lse, dK, dV, dQ, delta)
     check(load().cpa_share_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _ptr(O), _ptr(dO),
                                     _ptr(lse), _dtype_code(Q), B, H, L, D, N, rank_lo, rank_hi,
@@ -191,6 +244,11 @@ def zigzag_permute(src, pos_all, N: int, inverse: bool = False, rank_lo: int = 0
         if out is None:
             shape = (nr, B, H, Lr) if squeeze else (nr, B, H, Lr, D)
             out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    if inverse:
+        _expect(out, (B, H, L) if squeeze else (B, H, L, D), (src.dtype,), "out")
+    else:
+        _expect(out, (nr, B, H, Lr) if squeeze else (nr, B, H, Lr, D), (src.dtype,), "out")
+    _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _need_gpu(src, pos_all, out)
     check(load().cpa_zigzag_permute(_ptr(src), _ptr(out), src.element_size(), B, H, L, D,
                                     _ptr(pos_all), N, rank_lo, rank_hi, int(bool(inverse)),
@@ -205,6 +263,8 @@ def rope(x, pos, base: float = 10000.0, pairing: int = CPA_ROPE_INTERLEAVED, out
     B, H, rows, D = x.shape
     if out is None:
         out = torch.empty_like(x)
+    _expect(out, x.shape, (x.dtype,), "out")
+    _expect(pos, (rows,), (torch.int64,), "pos")
     _need_gpu(x, pos, out)
     check(load().cpa_rope(_ptr(x), _ptr(out), _dtype_code(x), B, H, rows, D, _ptr(pos),
                           float(base), int(pairing), _stream(x)))
@@ -221,6 +281,8 @@ def zigzag_permute_rope(src, pos_all, N: int, base: float = 10000.0,
     B, H, L, D = src.shape
     if out is None:
         out = torch.empty((rank_hi - rank_lo, B, H, L // N, D), dtype=src.dtype, device=src.device)
+    _expect(out, (rank_hi - rank_lo, B, H, L // max(N, 1), D), (src.dtype,), "out")
+    _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _need_gpu(src, pos_all, out)
     check(load().cpa_zigzag_permute_rope(_ptr(src), _ptr(out), _dtype_code(src), B, H, L, D,
                                          _ptr(pos_all), N, rank_lo, rank_hi, float(base),
@@ -235,6 +297,9 @@ def backward_delta(O, dO, out=None):
     rows = O.numel() // D
     if out is None:
         out = torch.empty(O.shape[:-1], dtype=torch.float32, device=O.device)
+    _expect(O, O.shape, (torch.float32,), "O")
+    _expect(dO, O.shape, (torch.bfloat16, torch.float32), "dO")
+    _expect(out, O.shape[:-1], (torch.float32,), "out")
     _need_gpu(O, dO, out)
     check(load().cpa_backward_delta(_ptr(O), _ptr(dO), _dtype_code(dO), rows, D, _ptr(out),
                                     _stream(O)))
@@ -245,8 +310,20 @@ def partial_backward(Q, K, V, dO, lse, delta, q_off, k_off, causal: bool, dQ, dK
                      scale: float = 0.0):
     """Add the gradient contributions of Q [B,H,Lq,D] against K/V [B,H,Lk,D]
     into the float32 accumulators dQ, dK, dV (one ring step of the backward)."""
+    torch = _torch()
     B, H, Lq, D = Q.shape
     Lk = K.shape[2]
+    dt, f32, i64 = (Q.dtype,), (torch.float32,), (torch.int64,)
+    _expect(K, (B, H, Lk, D), dt, "K")
+    _expect(V, (B, H, Lk, D), dt, "V")
+    _expect(dO, (B, H, Lq, D), dt, "dO")
+    _expect(lse, (B, H, Lq), f32, "lse")
+    _expect(delta, (B, H, Lq), f32, "delta")
+    _expect(q_off, (Lq,), i64, "q_off")
+    _expect(k_off, (Lk,), i64, "k_off")
+    _expect(dQ, (B, H, Lq, D), f32, "dQ")
+    _expect(dK, (B, H, Lk, D), f32, "dK")
+    _expect(dV, (B, H, Lk, D), f32, "dV")
     _need_gpu(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV)
     check(load().cpa_partial_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(lse), _ptr(delta),
                                       _dtype_code(Q), B, H, Lq, Lk, D, _ptr(q_off), _ptr(k_off),
@@ -265,6 +342,13 @@ def rank_backward(i: int, N: int, Q_i, K_all, V_all, pos_all, O_i, dO_i, lse_i, 
         dQ = torch.empty((B, H, Lr, D), dtype=torch.float32, device=Q_i.device)
     if delta is None:
         delta = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
+    _check_rank_major(Q_i, K_all, V_all, pos_all, N, O_i, lse_i)
+    f32 = (torch.float32,)
+    _expect(dO_i, (B, H, Lr, D), (Q_i.dtype,), "dO_i")
+    _expect(dK_all, (N, B, H, Lr, D), f32, "dK_all")
+    _expect(dV_all, (N, B, H, Lr, D), f32, "dV_all")
+    _expect(dQ, (B, H, Lr, D), f32, "dQ")
+    _expect(delta, (B, H, Lr), f32, "delta")
     _need_gpu(Q_i, K_all, V_all, pos_all, O_i, dO_i, lse_i, dK_all, dV_all, dQ, delta)
     check(load().cpa_rank_backward(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                    _ptr(O_i), _ptr(dO_i), _ptr(lse_i), _dtype_code(Q_i), B, H,

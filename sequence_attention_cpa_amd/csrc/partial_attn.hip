@@ -71,23 +71,6 @@ constexpr float LN2 = 0.6931471805599453f;
 // inputs with outlier rows, which rescale often.
 constexpr float RESCALE_LOG2 = 32.0f;
 
-// Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
-// K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
-// the order b = first + 1, first + 2, ..., first (mod nblk).  One block is one
-// ring step (cpa_partial); nblk = N with first = i is rank i's whole ring, the
-// running (O, max, sums) staying in registers from one block to the next.
-// Visiting the rank's own block last is deliberate: in every other block a
-// query tile sees either none of the keys or the same whole prefix as its
-// neighbours (the zigzag chunks do not interleave), so the workgroups of a
-// head sweep those blocks in step and share each K/V tile through L2; only
-// the own block gives every tile a different causal prefix, after which the
-// workgroups no longer run in step.
-//
-// GL (global layout): Q, K, V, O and lse are the whole sequence in global
-// token order, [BH, N * Lq, ...], and rank r's local row u lives at global row
-// zig(r, u) of the zigzag layout (chunk r for u < Lq/2, chunk 2N-1-r after),
-// so the zigzag permute is folded into the addressing.  The chunk length
-// Lq/2 is a multiple of 32, so every 32-row tile is contiguous in memory.
 // LDS layout of a 32-row K or V tile, in 16-byte slots, with column blocks
 // of W chunks (W = 4: 64-byte blocks, W = 8: 128-byte blocks): logical chunk
 // c of row r sits at slot 32W*(c/W) + W*r + ((c%W) ^ key(r)).  Column blocks
@@ -106,6 +89,23 @@ __device__ __forceinline__ int lds_slot(int r, int c) {
   return 32 * W * (c / W) + W * r + ((c % W) ^ lds_key<W>(r));
 }
 
+// Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
+// K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
+// the order b = first + 1, first + 2, ..., first (mod nblk).  One block is one
+// ring step (cpa_partial); nblk = N with first = i is rank i's whole ring, the
+// running (O, max, sums) staying in registers from one block to the next.
+// Visiting the rank's own block last is deliberate: in every other block a
+// query tile sees either none of the keys or the same whole prefix as its
+// neighbours (the zigzag chunks do not interleave), so the workgroups of a
+// head sweep those blocks in step and share each K/V tile through L2; only
+// the own block gives every tile a different causal prefix, after which the
+// workgroups no longer run in step.
+//
+// GL (global layout): Q, K, V, O and lse are the whole sequence in global
+// token order, [BH, N * Lq, ...], and rank r's local row u lives at global row
+// zig(r, u) of the zigzag layout (chunk r for u < Lq/2, chunk 2N-1-r after),
+// so the zigzag permute is folded into the addressing.  The chunk length
+// Lq/2 is a multiple of 32, so every 32-row tile is contiguous in memory.
 template <int D, bool GL>
 __global__ __launch_bounds__(NTHREADS, 2) void partial_attn_mfma_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,

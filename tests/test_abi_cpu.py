@@ -405,3 +405,41 @@ def _share_bwd(lib, **kw):
 def test_share_backward_rejects(lib, kw, status):
     assert _share_bwd(lib, **kw) == status
     assert cpa.last_error() != ""
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python layer checks every tensor's shape and dtype against the sizes
+    it passes to the library (which sees raw pointers), before any device use:
+    these CPU tensors never reach the GPU check."""
+    import torch
+    bf, f32, i64 = torch.bfloat16, torch.float32, torch.int64
+    B, H, L, N, D = 1, 2, 256, 4, 64
+    Lr = L // N
+    Q = torch.zeros(B, H, L, D, dtype=bf)
+    pos = torch.zeros(N, Lr, dtype=i64)
+    cases = [
+        (lambda: cpa.share_forward(Q, torch.zeros(B, H, L - 64, D, dtype=bf), Q, pos, N, True),
+         _lib.CPA_ESHAPE),
+        (lambda: cpa.share_forward(Q, torch.zeros(B, H, L, D, dtype=f32), Q, pos, N, True),
+         _lib.CPA_EDTYPE),
+        (lambda: cpa.share_forward(Q, Q, Q, pos, N, True, lse=torch.zeros(B, H, L - 1)),
+         _lib.CPA_ESHAPE),
+        (lambda: cpa.partial(Q[:, :, :Lr].contiguous(), Q, Q, pos[0], pos[1], True),
+         _lib.CPA_ESHAPE),
+        (lambda: cpa.rank_forward_fused(0, N, Q[:, :, :Lr].contiguous(),
+                                        torch.zeros(N, B, H, Lr, D, dtype=bf),
+                                        torch.zeros(N - 1, B, H, Lr, D, dtype=bf), pos, N, True),
+         _lib.CPA_ESHAPE),
+        (lambda: cpa.merge(torch.zeros(4, D), torch.zeros(4), torch.zeros(4, D, dtype=bf),
+                           torch.zeros(4)), _lib.CPA_EDTYPE),
+        (lambda: cpa.zigzag_permute(Q, pos, N, out=torch.zeros(N, B, H, Lr, D, dtype=f32)),
+         _lib.CPA_EDTYPE),
+        (lambda: cpa.rope(Q, torch.zeros(L - 1, dtype=i64)), _lib.CPA_ESHAPE),
+        (lambda: cpa.share_backward(Q, Q, Q, pos, torch.zeros(B, H, L, D), Q,
+                                    torch.zeros(B, H, L), N, True, torch.zeros(B, H, L, D),
+                                    torch.zeros(B, H, L, D, dtype=bf)), _lib.CPA_EDTYPE),
+    ]
+    for call, status in cases:
+        with pytest.raises(cpa.CpaError) as e:
+            call()
+        assert e.value.status == status, str(e.value)
