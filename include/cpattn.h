@@ -18,6 +18,11 @@
  *    [B, H, rows, D] with D fastest; "rank-major" data is [N, B, H, L/N, D].
  *  - Element types: cpa_dtype for Q/K/V; O and lse are always float32.
  *  - Device pointers must be 16-byte aligned (offset tables 8-byte aligned).
+ *  - Size limits (CPA_ESHAPE beyond them): B*H <= 65535; at most 2^30 rows
+ *    per query or key block; and a matrix-core launch (bf16, D = 64 or 128)
+ *    stays under 2^32 work-items: ceil(rows / 128) * B*H * 256 for the
+ *    forward and dQ passes, nblk * ceil(key rows / 128) * B*H * 512 for the
+ *    dK/dV pass of a ring over nblk blocks.
  *  - Ownership: the caller allocates and frees every buffer; the library
  *    keeps no pointer after a call returns and never allocates device memory.
  *  - Execution: every device call only enqueues work on `stream` (a

@@ -47,6 +47,8 @@ using namespace tile;
 
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr int BM = 128;        // query rows (dQ pass) or key rows (dK/dV pass) per workgroup
+static_assert(BM == cpa::kMfmaRows && NTHREADS == cpa::kMfmaThreads,
+              "the host checks launch sizes with these tile constants");
 constexpr float LOG2E = 1.4426950408889634f;
 
 using I0 = std::integral_constant<int, 0>;

@@ -8,6 +8,12 @@
 
 namespace cpa {
 
+// Launch shape of the matrix-core kernels (partial_attn.hip, attn_backward.hip
+// assert that they match): threads per workgroup, and query rows (forward, dQ
+// pass) or key rows (dK/dV pass, twice the threads) per workgroup.
+constexpr int kMfmaThreads = 256;
+constexpr int kMfmaRows = 128;
+
 // Partial attention, bf16 inputs on the matrix cores (D = 64 or 128).
 hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V,
                                const int64_t* q_off, const int64_t* k_off, float* O,

@@ -38,6 +38,31 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool supported_d(int32_t D) { return D == 16 || D == 64 || D == 128; }
 
+// The row kernels put the (b, h) pair in grid.y, which holds at most 65535
+// workgroups on every HIP target.
+constexpr int64_t kMaxBH = 65535;
+
+// A dispatch counts its work-items along x in 32 bits.  The matrix-core
+// kernels (bf16, D = 64 or 128) launch cpa::kMfmaThreads threads on every
+// cpa::kMfmaRows query rows of every (b, h) pair; the backward's dK/dV pass
+// launches twice that on every kMfmaRows key rows of every (b, h) pair and
+// K/V block.  nblk_bwd = 0 checks the forward launch only.
+cpa_status check_mfma_launch(cpa_dtype dt, int32_t D, int64_t BH, int64_t Lq, int64_t Lk,
+                             int64_t nblk_bwd) {
+  if (dt != CPA_BF16 || (D != 64 && D != 128)) return CPA_OK;
+  const int64_t lim = (int64_t)UINT32_MAX;
+  const int64_t qt = (Lq + cpa::kMfmaRows - 1) / cpa::kMfmaRows;
+  const int64_t kt = (Lk + cpa::kMfmaRows - 1) / cpa::kMfmaRows;
+  if (qt > lim / (BH * cpa::kMfmaThreads))
+    return fail(CPA_ESHAPE, "launch of %lld query rows x %lld heads exceeds 2^32 work-items",
+                (long long)Lq, (long long)BH);
+  if (nblk_bwd > 0 && kt > lim / (BH * 2 * cpa::kMfmaThreads) / nblk_bwd)
+    return fail(CPA_ESHAPE, "backward launch of %lld blocks x %lld key rows x %lld heads exceeds "
+                            "2^32 work-items",
+                (long long)nblk_bwd, (long long)Lk, (long long)BH);
+  return CPA_OK;
+}
+
 cpa_status check_partial(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
                          int32_t H, int64_t Lq, int64_t Lk, int32_t D, const int64_t* q_off,
                          const int64_t* k_off, int32_t causal, const float* O, const float* lse) {
@@ -47,7 +72,7 @@ cpa_status check_partial(const void* Q, const void* K, const void* V, cpa_dtype 
                                     (long long)Lq, (long long)Lk);
   if (Lq > (int64_t)1 << 30 || Lk > (int64_t)1 << 30)
     return fail(CPA_ESHAPE, "Lq and Lk are limited to 2^30 rows");
-  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
   if (!supported_d(D)) return fail(CPA_EUNSUPPORTED, "head_dim %d not built (16, 64, 128)", D);
   if (Lq > 0 && (!Q || !O || !lse)) return fail(CPA_EINVAL, "null Q/O/lse pointer");
   if (Lq > 0 && Lk > 0 && (!K || !V)) return fail(CPA_EINVAL, "null K/V pointer");
@@ -96,7 +121,7 @@ cpa_status check_rope(cpa_dtype dt, int32_t B, int32_t H, int32_t D, double base
                       int32_t pairing) {
   if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
   if (B < 1 || H < 1) return fail(CPA_ESHAPE, "B and H must be >= 1 (B=%d, H=%d)", B, H);
-  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
   if (D < 8 || D > 512 || D % 8 != 0)
     return fail(CPA_EUNSUPPORTED, "rope needs D a multiple of 8 in [8, 512] (D=%d)", D);
   if (!(base > 1.0) || !std::isfinite(base))
@@ -139,6 +164,7 @@ cpa_status cpa_partial(const void* Q, const void* K, const void* V, cpa_dtype dt
                        void* stream) {
   cpa_status st = check_partial(Q, K, V, dt, B, H, Lq, Lk, D, q_off, k_off, causal, O, lse);
   if (st != CPA_OK) return st;
+  if (Lk > 0 && (st = check_mfma_launch(dt, D, (int64_t)B * H, Lq, Lk, 0)) != CPA_OK) return st;
   return enqueue_partial(Q, K, V, dt, B, H, Lq, Lk, D, q_off, k_off, causal, scale, O, lse,
                          (hipStream_t)stream);
 }
@@ -173,6 +199,8 @@ cpa_status cpa_rank_forward(int32_t i, int32_t N, const void* Q_i, const void* K
   if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
   const int64_t Lr = L / N;
   st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, O_i, lse_i);
+  if (st != CPA_OK) return st;
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, 0);
   if (st != CPA_OK) return st;
   const size_t need = cpa_rank_forward_workspace(B, H, L, N, D);
   if (N > 1) {
@@ -218,6 +246,8 @@ cpa_status cpa_rank_forward_fused(int32_t i, int32_t N, const void* Q_i, const v
   if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
   const int64_t Lr = L / N;
   st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, O_i, lse_i);
+  if (st != CPA_OK) return st;
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, 0);
   if (st != CPA_OK) return st;
   if (dt != CPA_BF16 || (D != 64 && D != 128))
     return fail(CPA_EUNSUPPORTED, "fused ring needs bf16 with D = 64 or 128 (use cpa_rank_forward)");
@@ -298,7 +328,9 @@ cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, const 
                                   "of 32 (L=%lld, N=%d); use the rank-major path",
                 (long long)L, N);
   if (Lr > ((int64_t)1 << 30)) return fail(CPA_ESHAPE, "L/N is limited to 2^30 rows");
-  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, 0);
+  if (st != CPA_OK) return st;
   if (!Q || !K || !V || !pos_all || !O || !lse) return fail(CPA_EINVAL, "null pointer");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
     return fail(CPA_EINVAL, "Q, K, V and O must be 16-byte aligned");
@@ -335,6 +367,8 @@ cpa_status cpa_partial_backward(const void* Q, const void* K, const void* V, con
   cpa_status st = check_partial(Q, K, V, dt, B, H, Lq, Lk, D, q_off, k_off, causal, dQ, lse);
   if (st != CPA_OK) return st;
   if (Lq == 0 || Lk == 0) return ok();  // no pair: every contribution is zero
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lq, Lk, 1);
+  if (st != CPA_OK) return st;
   if (!dO || !delta || !dK || !dV) return fail(CPA_EINVAL, "null dO/delta/dK/dV pointer");
   if (!aligned(dO, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(delta, 4))
     return fail(CPA_EINVAL, "dO, dK and dV must be 16-byte aligned, delta 4-byte");
@@ -364,6 +398,8 @@ cpa_status cpa_rank_backward(int32_t i, int32_t N, const void* Q_i, const void* 
   if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
   st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, dQ_i,
                      lse_i);
+  if (st != CPA_OK) return st;
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, N);
   if (st != CPA_OK) return st;
   if (!O_i || !dO_i || !dK_all || !dV_all || !delta_i)
     return fail(CPA_EINVAL, "null O/dO/dK/dV/delta pointer");
@@ -414,7 +450,9 @@ cpa_status cpa_share_backward(const void* Q, const void* K, const void* V, const
                                   "multiples of 32 (L=%lld, N=%d); use the rank-major path",
                 (long long)L, N);
   if (Lr > ((int64_t)1 << 30)) return fail(CPA_ESHAPE, "L/N is limited to 2^30 rows");
-  if ((int64_t)B * H > (1 << 24)) return fail(CPA_ESHAPE, "B*H is limited to 2^24");
+  if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, N);
+  if (st != CPA_OK) return st;
   if (!Q || !K || !V || !pos_all || !O || !dO || !lse || !dQ || !dK || !dV || !delta)
     return fail(CPA_EINVAL, "null pointer");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||

@@ -63,6 +63,8 @@ constexpr int BM = 128;        // query rows per workgroup
 constexpr int NKB = BN / 32;   // 32-key MFMA blocks per tile
 static_assert(NKB == 1, "the LDS tile layout holds 32 rows");
 constexpr int NTHREADS = 256;  // 4 waves
+static_assert(BM == cpa::kMfmaRows && NTHREADS == cpa::kMfmaThreads,
+              "the host checks launch sizes with these tile constants");
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 // Lazy-rescale threshold (log2 units).  P stays below 2^33, exact in bf16

@@ -102,6 +102,8 @@ def _partial(lib, **kw):
     (dict(H=-1), _lib.CPA_ESHAPE),
     (dict(Lq=-1), _lib.CPA_ESHAPE),
     (dict(Lk=(1 << 30) + 1), _lib.CPA_ESHAPE),
+    (dict(B=256, H=256), _lib.CPA_ESHAPE),            # B*H above the 65535 grid.y bound
+    (dict(Lq=1 << 30, H=64), _lib.CPA_ESHAPE),        # 2^37 work-items in one launch
     (dict(Q=None), _lib.CPA_EINVAL),
     (dict(V=None), _lib.CPA_EINVAL),
     (dict(lse=None), _lib.CPA_EINVAL),
@@ -307,6 +309,8 @@ def _pbwd(lib, **kw):
     (dict(D=48), _lib.CPA_EUNSUPPORTED),
     (dict(Lq=-2), _lib.CPA_ESHAPE),
     (dict(H=0), _lib.CPA_ESHAPE),
+    (dict(B=300, H=300), _lib.CPA_ESHAPE),
+    (dict(Lk=1 << 30, H=64), _lib.CPA_ESHAPE),        # dK/dV pass: 2^38 work-items
     (dict(Q=None), _lib.CPA_EINVAL),
     (dict(dO=None), _lib.CPA_EINVAL),
     (dict(delta=None), _lib.CPA_EINVAL),
@@ -345,6 +349,7 @@ def _rbwd(lib, **kw):
     (dict(delta=None), _lib.CPA_EINVAL),
     (dict(dK=P + 4), _lib.CPA_EINVAL),
     (dict(lse=None), _lib.CPA_EINVAL),
+    (dict(N=1 << 23, L=1 << 31), _lib.CPA_ESHAPE),   # 2^23 blocks: dK/dV launch over 2^32
 ])
 def test_rank_backward_rejects(lib, kw, status):
     assert _rbwd(lib, **kw) == status
@@ -370,6 +375,8 @@ def _share(lib, **kw):
     (dict(N=0), _lib.CPA_EINVAL),
     (dict(lo=2, hi=1), _lib.CPA_EINVAL),
     (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(B=2, H=32768), _lib.CPA_ESHAPE),
+    (dict(L=1 << 30, H=64), _lib.CPA_ESHAPE),        # 2^28 rows per rank x 64 heads
     (dict(O=P + 4), _lib.CPA_EINVAL),
 ])
 def test_share_forward_rejects(lib, kw, status):
@@ -401,6 +408,7 @@ def _share_bwd(lib, **kw):
     (dict(O=None), _lib.CPA_EINVAL),
     (dict(dK=P + 4), _lib.CPA_EINVAL),
     (dict(lse=P + 2), _lib.CPA_EINVAL),
+    (dict(N=1 << 22, L=1 << 28), _lib.CPA_ESHAPE),   # 2^22 blocks x 2 heads x 512 threads
 ])
 def test_share_backward_rejects(lib, kw, status):
     assert _share_bwd(lib, **kw) == status
