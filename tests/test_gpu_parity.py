@@ -372,7 +372,13 @@ def test_rank_forward_fused_small_shapes(case):
     assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
 
 
-SHARE_CASES = [c for c in FUSED_CASES if (c[2] // c[3] // 2) % 32 == 0]
+SHARE_CASES = [c for c in FUSED_CASES if (c[2] // c[3] // 2) % 32 == 0] + [
+    # chunks that are not multiples of the 128-row workgroup: a workgroup's
+    # waves straddle the rank's two chunks, and the last one is partial
+    (1, 2, 768, 4, 128, True),    # C = 96
+    (2, 2, 320, 5, 64, True),     # C = 32, one 64-row workgroup per rank
+    (1, 1, 1280, 4, 128, True),   # C = 160
+]
 
 
 @pytest.mark.parametrize("case", SHARE_CASES, ids=[str(c) for c in SHARE_CASES])
