@@ -21,14 +21,14 @@
 //    dQ^T += K^T dS^T with K^T read from LDS by ds_read_b64_tr_b16.  The lse
 //    is known, so there is no running max and no rescaling.  The pass walks
 //    the N blocks of a ring in one launch (same order as the forward).
-//  * dK/dV pass: roles swapped.  A workgroup owns 128 keys (32 per wave, K and
-//    V rows in registers); Q and dO tiles of 32 queries stream through LDS,
-//    with their lse and delta.  Per tile: S = Q K^T and dP = dO V^T (each lane
-//    holds 16 queries of ONE key), P and dS, then dV^T += dO^T P and
-//    dK^T += Q^T dS with the transposed operands read by ds_read_b64_tr_b16.
-//    The accumulators of both gradients and the resident K/V rows need about
-//    260 registers per lane, so this pass runs one wave per SIMD (the
-//    accumulators may live in AGPRs).
+//  * dK/dV pass: roles swapped.  A workgroup owns 128 keys; Q and dO tiles of
+//    32 queries stream through LDS, with their lse and delta.  Per tile:
+//    S = Q K^T and dP = dO V^T (each lane holds 16 queries of ONE key), P and
+//    dS, then dV^T += dO^T P and dK^T += Q^T dS with the transposed operands
+//    read by ds_read_b64_tr_b16.  Both accumulators and both resident K/V
+//    rows would need about 260 registers per lane, so two waves share each
+//    32-key group and split its products (P role: S, P and dV; dS role: dP,
+//    dS and dK), which keeps two waves per SIMD.
 // Causal visibility compares global positions (key position <= query
 // position); positions increase inside every block, so a query's visible keys
 // are a prefix of a block and a key's visible queries a suffix; only tiles
