@@ -150,6 +150,53 @@ def test_ring_backward_all_ranks(case):
         say(f"ring bwd {case} {name}: {e[0]:.3e} {e[1]:.3e}")
 
 
+def peaked(shape, seed):
+    """bf16 Q or K with every 7th / 5th row scaled by 8: scores in the
+    hundreds on those rows, so many softmax rows are dominated by one key."""
+    Q = rand(shape, torch.float32, seed)
+    K = rand(shape, torch.float32, seed + 1)
+    Q[:, :, ::7] *= 8
+    K[:, :, ::5] *= 8
+    return Q.to(torch.bfloat16), K.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_partial_backward_large_logits(D):
+    """One causal block with outlier-sized scores: P = exp(s - lse) cancels
+    two numbers in the hundreds, and dS is dominated by single keys."""
+    B, H, L = 1, 2, 320
+    Q, K = peaked((B, H, L, D), 140)
+    V, dO = rand((B, H, L, D), torch.bfloat16, 142), rand((B, H, L, D), torch.bfloat16, 143)
+    off = np.arange(L, dtype=np.int64)
+    Q64, K64, V64, dO64 = (widen(x) for x in (Q, K, V, dO))
+    O, lse = cpa_oracle.partial(Q64, K64, V64, off, off, True)
+    delta = cpa_oracle.backward_delta(O, dO64)
+    ref = cpa_oracle.partial_backward(Q64, K64, V64, dO64, lse, delta, off, off, True)
+    acc = [torch.zeros(x.shape, dtype=torch.float32, device=DEV) for x in (Q, K, V)]
+    offd = torch.from_numpy(off).to(DEV)
+    delta_d = cpa.backward_delta(torch.from_numpy(O).float().to(DEV), dO.to(DEV))
+    cpa.partial_backward(Q.to(DEV), K.to(DEV), V.to(DEV), dO.to(DEV),
+                         torch.from_numpy(lse).float().to(DEV), delta_d, offd, offd, True, *acc)
+    torch.cuda.synchronize()
+    for name, a, r in zip(("dQ", "dK", "dV"), acc, ref):
+        e = assert_grad_close(a.cpu().double().numpy(), r, True, f"large logits D={D} {name}")
+        say(f"partial bwd large logits D={D} {name}: {e[0]:.3e} {e[1]:.3e}")
+
+
+@pytest.mark.parametrize("mode", [True, "global"])
+def test_ring_backward_large_logits(mode):
+    """Forward then backward of every rank with outlier-sized scores: the
+    backward uses the lse the GPU forward produced (lazy rescale included)."""
+    B, H, L, N, D = 1, 2, 2048, 4, 128
+    Q, K = peaked((B, H, L, D), 150)
+    V, dO = rand((B, H, L, D), torch.bfloat16, 152), rand((B, H, L, D), torch.bfloat16, 153)
+    got = run_pipeline(Q, K, V, dO, N, True, mode)
+    ref = cpa_oracle.attention_backward(widen(Q), widen(K), widen(V), widen(dO), True)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        e = assert_grad_close(g, r, True, f"large logits {mode} {name}")
+        say(f"ring bwd large logits {mode} {name}: {e[0]:.3e} {e[1]:.3e}")
+
+
 def oracle_backward_heads(Q, K, V, dO, heads, causal=True):
     """attention_backward of selected (b, h) heads, spread over host threads."""
     def one(bh):
