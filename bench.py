@@ -193,10 +193,14 @@ def main():
     # Per-kernel timing on the same stream: the global-layout launch, the fused
     # ring launch on rank-major data, the unfused ring's partials (same kernel
     # and arguments as inside cpa_rank_forward), a merge, and the K permute.
+    # The rank-major forms need rank-major buffers, which a global-layout
+    # pipeline does not hold: a rank-major pipeline provides them.
+    rk = pipe if not pipe.global_layout else SharePipeline(
+        w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, dev, rank, rank + 1, fused=True)
     zigzag = cpa.zigzag_permute
-    zigzag(K, pipe.pos, w.N, out=pipe.Kr)
-    zigzag(V, pipe.pos, w.N, out=pipe.Vr)
-    zigzag(Q, pipe.pos, w.N, rank_lo=rank, rank_hi=rank + 1, out=pipe.Qr)
+    zigzag(K, pipe.pos, w.N, out=rk.Kr)
+    zigzag(V, pipe.pos, w.N, out=rk.Vr)
+    zigzag(Q, pipe.pos, w.N, rank_lo=rank, rank_hi=rank + 1, out=rk.Qr)
     Lr = w.Lr
     tO = torch.empty((w.B, w.H, Lr, w.D), dtype=torch.float32, device=dev)
     tl = torch.empty((w.B, w.H, Lr), dtype=torch.float32, device=dev)
@@ -220,23 +224,23 @@ def main():
                                                     lse=pipe.lse), reps)
     fused_evs, last_evs = [], []
     if mfma_ok:
-        fused_evs = timed(lambda: cpa.rank_forward_fused(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr,
+        fused_evs = timed(lambda: cpa.rank_forward_fused(rank, w.N, rk.Qr[0], rk.Kr, rk.Vr,
                                                          pos_d, w.causal, out=tO, lse=tl), reps)
         # Balance: the last rank's ring does the same causal work under zigzag.
         other = w.N - 1 if rank != w.N - 1 else 0
         Q_other = cpa.zigzag_permute(Q, pos_d, w.N, rank_lo=other, rank_hi=other + 1)[0]
-        last_evs = timed(lambda: cpa.rank_forward_fused(other, w.N, Q_other, pipe.Kr, pipe.Vr,
+        last_evs = timed(lambda: cpa.rank_forward_fused(other, w.N, Q_other, rk.Kr, rk.Vr,
                                                         pos_d, w.causal, out=tO, lse=tl), reps)
     part_evs = []
     for _ in range(reps):
         for s in range(w.N):
             j = (rank + s) % w.N
             part_evs += [(j, e) for e in timed(lambda: cpa.partial(
-                pipe.Qr[0], pipe.Kr[j], pipe.Vr[j], pos_d[rank], pos_d[j], w.causal, out=tO,
+                rk.Qr[0], rk.Kr[j], rk.Vr[j], pos_d[rank], pos_d[j], w.causal, out=tO,
                 lse=tl), 1)]
-    mevs = timed(lambda: cpa.merge(pipe.Or[0], pipe.lser[0], tO, tl), reps)
-    pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=pipe.Kr), reps)
-    rope_evs = timed(lambda: cpa.zigzag_permute_rope(K, pos_d, w.N, 10000.0, out=pipe.Kr), reps)
+    mevs = timed(lambda: cpa.merge(rk.Or[0], rk.lser[0], tO, tl), reps)
+    pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=rk.Kr), reps)
+    rope_evs = timed(lambda: cpa.zigzag_permute_rope(K, pos_d, w.N, 10000.0, out=rk.Kr), reps)
     # Ring backward of the same rank (delta + dQ pass + dK/dV pass), after a
     # forward step so that O and lse are the ring's: on global-order data
     # (cpa_share_backward, the pipeline's backward in the default mode) and on
@@ -250,16 +254,16 @@ def main():
             gbwd_evs = timed(lambda: cpa.share_backward(
                 Q, K, V, pos_d, pipe.O, dO, pipe.lse, w.N, w.causal, pipe.dK, pipe.dV,
                 pipe.scale, rank, rank + 1, dQ=pipe.dQ, delta=pipe.delta), reps)
-        zigzag(pipe.O, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=pipe.Or)
-        zigzag(pipe.lse, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=pipe.lser)
+        zigzag(pipe.O, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=rk.Or)
+        zigzag(pipe.lse, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=rk.lser)
         dOr = zigzag(dO, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1)
         f32 = dict(dtype=torch.float32, device=dev)
         dQr = torch.empty((w.B, w.H, Lr, w.D), **f32)
         deltar = torch.empty((w.B, w.H, Lr), **f32)
-        dKr = torch.zeros(pipe.Kr.shape, **f32)
-        dVr = torch.zeros(pipe.Vr.shape, **f32)
-        bwd_evs = timed(lambda: cpa.rank_backward(rank, w.N, pipe.Qr[0], pipe.Kr, pipe.Vr, pos_d,
-                                                  pipe.Or[0], dOr[0], pipe.lser[0], w.causal,
+        dKr = torch.zeros(rk.Kr.shape, **f32)
+        dVr = torch.zeros(rk.Vr.shape, **f32)
+        bwd_evs = timed(lambda: cpa.rank_backward(rank, w.N, rk.Qr[0], rk.Kr, rk.Vr, pos_d,
+                                                  rk.Or[0], dOr[0], rk.lser[0], w.causal,
                                                   dKr, dVr, pipe.scale, dQ=dQr, delta=deltar),
                         reps)
     torch.cuda.synchronize()

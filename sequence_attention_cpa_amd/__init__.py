@@ -8,8 +8,9 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (CPA_BF16, CPA_EDTYPE, CPA_ESHAPE, CPA_F32, CPA_ROPE_HALF,  # noqa: F401
-                   CPA_ROPE_INTERLEAVED, CpaError, check, last_error, load, version)
+from ._lib import (CPA_BF16, CPA_EDTYPE, CPA_EINVAL, CPA_ESHAPE, CPA_F32,  # noqa: F401
+                   CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED, CpaError, check, last_error, load,
+                   version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
            "rank_forward_fused", "share_forward", "share_backward", "zigzag_permute", "rope",
@@ -28,7 +29,7 @@ def _dtype_code(t):
         return CPA_BF16
     if t.dtype == torch.float32:
         return CPA_F32
-    raise CpaError(3, f"unsupported tensor dtype {t.dtype} (bfloat16 or float32)")
+    raise CpaError(CPA_EDTYPE, f"unsupported tensor dtype {t.dtype} (bfloat16 or float32)")
 
 
 def _ptr(t):
@@ -56,9 +57,9 @@ def _need_gpu(*ts):
         if t is None:
             continue
         if not t.is_cuda:
-            raise CpaError(1, "tensors must live on the GPU")
+            raise CpaError(CPA_EINVAL, "tensors must live on the GPU")
         if not t.is_contiguous():
-            raise CpaError(1, "tensors must be contiguous")
+            raise CpaError(CPA_EINVAL, "tensors must be contiguous")
 
 
 def zigzag_layout(L: int, N: int):

@@ -29,7 +29,9 @@ global-order tensors instead (no permutes).  With RoPE the returned dQ, dK
 are gradients with respect to the rotated Q, K.
 
 All buffers are allocated once in the constructor (the backward's on first
-use); `step` and `backward` allocate nothing after that.
+use); `step` and `backward` allocate nothing after that.  The global-layout
+mode allocates no rank-major buffers: only O, lse and (for the backward) the
+global-order gradients and delta.
 """
 from __future__ import annotations
 
@@ -55,15 +57,17 @@ class SharePipeline:
         self.rank_hi = N if rank_hi is None else rank_hi
         nr = self.rank_hi - self.rank_lo
         Lr = L // N
+        self.device = device
         self.pos_host = zigzag_layout(L, N)
         self.pos = self.pos_host.to(device)
-        self.Kr = torch.empty((N, B, H, Lr, D), dtype=dtype, device=device)
-        self.Vr = torch.empty_like(self.Kr)
-        self.Qr = torch.empty((nr, B, H, Lr, D), dtype=dtype, device=device)
-        self.Or = torch.empty((nr, B, H, Lr, D), dtype=torch.float32, device=device)
-        self.lser = torch.empty((nr, B, H, Lr), dtype=torch.float32, device=device)
-        ws_bytes = 1 if fused else max(rank_forward_workspace(B, H, L, N, D), 1)
-        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        if not global_layout:
+            self.Kr = torch.empty((N, B, H, Lr, D), dtype=dtype, device=device)
+            self.Vr = torch.empty_like(self.Kr)
+            self.Qr = torch.empty((nr, B, H, Lr, D), dtype=dtype, device=device)
+            self.Or = torch.empty((nr, B, H, Lr, D), dtype=torch.float32, device=device)
+            self.lser = torch.empty((nr, B, H, Lr), dtype=torch.float32, device=device)
+            ws_bytes = 1 if fused else max(rank_forward_workspace(B, H, L, N, D), 1)
+            self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.O = torch.zeros((B, H, L, D), dtype=torch.float32, device=device)
         self.lse = torch.full((B, H, L), float("-inf"), dtype=torch.float32, device=device)
 
@@ -106,7 +110,7 @@ class SharePipeline:
         import torch
 
         N, lo, hi = self.N, self.rank_lo, self.rank_hi
-        f32 = dict(dtype=torch.float32, device=self.Kr.device)
+        f32 = dict(dtype=torch.float32, device=self.device)
         if not hasattr(self, "dQ"):
             self.dQ = torch.zeros((self.B, self.H, self.L, self.D), **f32)
             self.dK = torch.empty_like(self.dQ)
