@@ -231,6 +231,22 @@ def main():
         Q_other = cpa.zigzag_permute(Q, pos_d, w.N, rank_lo=other, rank_hi=other + 1)[0]
         last_evs = timed(lambda: cpa.rank_forward_fused(other, w.N, Q_other, rk.Kr, rk.Vr,
                                                         pos_d, w.causal, out=tO, lse=tl), reps)
+    # Balance without the zigzag: the same one-launch ring on a contiguous split
+    # (rank r holds tokens [r L/N, (r+1) L/N)), first and last rank.  Under the
+    # causal mask the last rank meets (2N-1) times the first rank's pairs, and a
+    # CP step waits for the slowest rank.
+    contig = {}
+    if mfma_ok and w.causal and w.N > 1:
+        pos_c = torch.arange(w.L, dtype=torch.int64, device=dev).reshape(w.N, Lr)
+        pos_ch = pos_c.cpu().numpy()
+        Kc = zigzag(K, pos_c, w.N)
+        Vc = zigzag(V, pos_c, w.N)
+        for r in (0, w.N - 1):
+            Qc = zigzag(Q, pos_c, w.N, rank_lo=r, rank_hi=r + 1)[0]
+            evs = timed(lambda: cpa.rank_forward_fused(r, w.N, Qc, Kc, Vc, pos_c, True, out=tO,
+                                                       lse=tl), reps)
+            contig[r] = (evs, sum(causal_pairs(pos_ch[r], pos_ch[j]) for j in range(w.N)))
+        del Kc, Vc
     part_evs = []
     for _ in range(reps):
         for s in range(w.N):
@@ -305,6 +321,20 @@ def main():
                 "useful_flop": b_flop}
     bwd = bwd_report(bwd_evs)
     gbwd = bwd_report(gbwd_evs)
+    balance = None
+    if contig and o_ms is not None and rank == 0:
+        c0, cl = (float(np.median([a.elapsed_time(b) for a, b in contig[r][0]]))
+                  for r in (0, w.N - 1))
+        z0, zl = float(np.median(f_ms)), float(np.median(o_ms))
+        # Per-rank work is linear in the rank under either split, so the mean
+        # over ranks is the mean of the first and the last.
+        balance = {"contiguous_ms": [round(c0, 4), round(cl, 4)],
+                   "contiguous_pairs": [contig[0][1], contig[w.N - 1][1]],
+                   "contiguous_step_efficiency": round((c0 + cl) / 2 / max(c0, cl), 3),
+                   "zigzag_ms": [round(z0, 4), round(zl, 4)],
+                   "zigzag_pairs": [sum(pairs), sum(
+                       causal_pairs(pos[w.N - 1], pos[j]) for j in range(w.N))],
+                   "zigzag_step_efficiency": round((z0 + zl) / 2 / max(z0, zl), 3)}
 
     value = useful / (ms_step * 1e-3) / 1e12
     out = {
@@ -349,6 +379,7 @@ def main():
                                "bytes": perm_bytes},
             "ms_per_step_events": round(ms_step_ev, 4),
             "step_ms_stats": stats(step_ms),
+            "balance_first_last_rank": balance,
             "rank_backward": bwd,
             "share_backward": gbwd,
         },
