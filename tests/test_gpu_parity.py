@@ -372,6 +372,27 @@ def test_rank_forward_fused_small_shapes(case):
     assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_rank_forward_fused_contiguous_split(D):
+    """The one-launch ring takes any increasing position table: a contiguous
+    split (rank r holds tokens [r L/N, (r+1) L/N), the unbalanced layout the
+    zigzag replaces) gives every rank its rows of whole-sequence attention."""
+    B, H, L, N = 1, 2, 2048, 4
+    Lr = L // N
+    Q, K, V = (rand((B, H, L, D), torch.bfloat16, 70 + i) for i in range(3))
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), True)
+    pos = torch.arange(L, dtype=torch.int64).reshape(N, Lr).to(DEV)
+    Kc = cpa.zigzag_permute(K.to(DEV), pos, N)
+    Vc = cpa.zigzag_permute(V.to(DEV), pos, N)
+    Qc = cpa.zigzag_permute(Q.to(DEV), pos, N)
+    for r in range(N):
+        O, lse = cpa.rank_forward_fused(r, N, Qc[r], Kc, Vc, pos, True)
+        torch.cuda.synchronize()
+        rows = slice(r * Lr, (r + 1) * Lr)
+        assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(),
+                          Or[:, :, rows], lr[:, :, rows], f"contiguous rank {r} D={D}")
+
+
 SHARE_CASES = [c for c in FUSED_CASES if (c[2] // c[3] // 2) % 32 == 0] + [
     # chunks that are not multiples of the 128-row workgroup: a workgroup's
     # waves straddle the rank's two chunks, and the last one is partial
