@@ -451,3 +451,34 @@ def test_binding_rejects_mismatched_tensors():
         with pytest.raises(cpa.CpaError) as e:
             call()
         assert e.value.status == status, str(e.value)
+
+
+def test_error_text_is_per_thread():
+    """Two host threads fail different calls in lockstep: each reads back its
+    own message, and a successful call clears it (the header's promise)."""
+    import threading
+
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, call, want):
+        texts = []
+        for _ in range(50):
+            assert call() != _lib.CPA_OK
+            barrier.wait()  # both threads have failed before either reads
+            texts.append(cpa.last_error())
+            barrier.wait()
+        out = (ctypes.c_int64 * 64)()
+        assert lib_ok.cpa_zigzag_layout(64, 4, out) == _lib.CPA_OK
+        seen[name] = (texts, cpa.last_error(), want)
+
+    lib_ok = _lib.load()
+    t1 = threading.Thread(target=worker, args=(
+        "layout", lambda: lib_ok.cpa_zigzag_layout(62, 4, (ctypes.c_int64 * 64)()), "2N"))
+    t2 = threading.Thread(target=worker, args=(
+        "merge", lambda: lib_ok.cpa_merge(P, P, P, P, 10, 48, None), "head_dim"))
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert set(seen) == {"layout", "merge"}
+    for name, (texts, after, want) in seen.items():
+        assert all(want in t for t in texts), f"{name}: {set(texts)}"
+        assert after == "", f"{name}: error text not cleared by a successful call"
