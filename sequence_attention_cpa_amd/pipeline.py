@@ -14,11 +14,13 @@ N partial launches and N-1 merges; bf16 with D = 64 or 128 only.
 With `global_layout=True` the whole step is one cpa_share_forward call per
 rank: the kernel reads global-order Q/K/V and writes global-order O/lse,
 with the zigzag permute folded into its addressing (bf16, D = 64 or 128,
-chunks L/(2N) a multiple of 32, no RoPE).
+chunks L/(2N) a multiple of 32).
 
-With `rope_base` set, Q and K are rotated at their global positions on the
+With `rope_base` set, Q and K are rotated at their global positions: on the
 way into rank-major order (cpa_zigzag_permute_rope: the rotary embedding is
-folded into the permute, so it costs no extra pass over memory).
+folded into the permute, so it costs no extra pass over memory), or, in
+global-layout mode, by cpa_rope into rotated global-order copies (positions
+0 .. L-1) that the ring then reads.
 
 `backward(dO)` runs the ring backward of the ranks after a `step`: dO is
 permuted like Q, each rank's cpa_rank_backward writes its dQ and adds its
@@ -36,7 +38,7 @@ global-order gradients and delta.
 from __future__ import annotations
 
 from . import (CPA_ROPE_INTERLEAVED, rank_backward, rank_forward, rank_forward_fused,
-               rank_forward_workspace, share_backward, share_forward, zigzag_layout,
+               rank_forward_workspace, rope, share_backward, share_forward, zigzag_layout,
                zigzag_permute, zigzag_permute_rope)
 
 
@@ -51,8 +53,6 @@ class SharePipeline:
         self.causal, self.scale, self.fused = causal, scale, fused
         self.rope_base, self.rope_pairing = rope_base, rope_pairing
         self.global_layout = global_layout
-        if global_layout and rope_base is not None:
-            raise ValueError("the global-layout step has no RoPE; rotate Q/K first (cpa_rope)")
         self.rank_lo = rank_lo
         self.rank_hi = N if rank_hi is None else rank_hi
         nr = self.rank_hi - self.rank_lo
@@ -68,6 +68,10 @@ class SharePipeline:
             self.lser = torch.empty((nr, B, H, Lr), dtype=torch.float32, device=device)
             ws_bytes = 1 if fused else max(rank_forward_workspace(B, H, L, N, D), 1)
             self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        elif rope_base is not None:
+            self.pos_glob = torch.arange(L, dtype=torch.int64, device=device)
+            self.Qrot = torch.empty((B, H, L, D), dtype=dtype, device=device)
+            self.Krot = torch.empty_like(self.Qrot)
         self.O = torch.zeros((B, H, L, D), dtype=torch.float32, device=device)
         self.lse = torch.full((B, H, L), float("-inf"), dtype=torch.float32, device=device)
 
@@ -76,6 +80,10 @@ class SharePipeline:
         rows of ranks outside [rank_lo, rank_hi) are left as initialised."""
         N, lo, hi = self.N, self.rank_lo, self.rank_hi
         if self.global_layout:
+            if self.rope_base is not None:
+                rope(Q, self.pos_glob, self.rope_base, self.rope_pairing, out=self.Qrot)
+                rope(K, self.pos_glob, self.rope_base, self.rope_pairing, out=self.Krot)
+                Q, K = self.Qrot, self.Krot
             self._inputs = (Q, K, V)
             share_forward(Q, K, V, self.pos, N, self.causal, self.scale, lo, hi, out=self.O,
                           lse=self.lse)

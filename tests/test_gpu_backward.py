@@ -331,3 +331,20 @@ def test_share_backward_rank_subset():
     assert np.all(dQ[:, :, np.concatenate([p[0], p[3]])] == 7.0), "other ranks' dQ rows changed"
     assert_grad_close(dK, dK_ref, True, "dK of ranks 1-2")
     assert_grad_close(dV, dV_ref, True, "dV of ranks 1-2")
+
+
+@pytest.mark.parametrize("mode", [True, "global"])
+def test_ring_backward_with_rope(mode):
+    """With RoPE the pipeline's dQ and dK are gradients with respect to the
+    rotated Q and K: against the oracle's backward on inputs rotated at their
+    global positions (fp64 rotation, rounded to bf16 as the kernels see them)."""
+    B, H, L, N, D = 1, 2, 2048, 4, 128
+    Q, K, V, dO = (rand((B, H, L, D), torch.bfloat16, 160 + i) for i in range(4))
+    got = run_pipeline(Q, K, V, dO, N, True, mode, rope=10000.0)
+    pos = np.arange(L)
+    Qr, Kr = (torch.from_numpy(cpa_oracle.rope(widen(x), pos, 10000.0, cpa.CPA_ROPE_INTERLEAVED))
+              .to(torch.bfloat16) for x in (Q, K))
+    ref = cpa_oracle.attention_backward(widen(Qr), widen(Kr), widen(V), widen(dO), True)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        e = assert_grad_close(g, r, True, f"rope {mode} {name}")
+        say(f"ring bwd rope {mode} {name}: {e[0]:.3e} {e[1]:.3e}")

@@ -143,9 +143,10 @@ def test_rope_pipeline_12k_every_row(pairing):
     say("12k rope: generating")
     Q, K, V, _ = make_inputs(w)
     outs = {}
-    for fused in (False, True):
-        pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=fused,
-                             rope_base=10000.0, rope_pairing=pairing)
+    for fused in (False, True, "global"):
+        pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, fused=bool(fused),
+                             rope_base=10000.0, rope_pairing=pairing,
+                             global_layout=fused == "global")
         O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
         torch.cuda.synchronize()
         outs[fused] = (O.cpu().double().numpy(), lse.cpu().double().numpy())
@@ -162,15 +163,17 @@ def test_rope_pipeline_12k_every_row(pairing):
         say(f"12k rope pairing={pairing} fused={fused}: max {mx:.3e} mean {mean:.3e}")
 
 
-def test_rope_pipeline_128k_share_sampled():
+@pytest.mark.parametrize("mode", ["fused", "global"])
+def test_rope_pipeline_128k_share_sampled(mode):
     """128k share (rank 3: positions 49152-65535 and 65536-81919) with RoPE,
-    one fused launch, sampled rows against the oracle."""
+    one ring launch on rank-major or global-order data, sampled rows against
+    the oracle."""
     w = WORKLOADS["128k"]
     rank = 3
-    say("128k rope: generating")
+    say(f"128k rope {mode}: generating")
     Q, K, V, outl = make_inputs(w)
     pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, rank, rank + 1,
-                         fused=True, rope_base=10000.0)
+                         fused=True, rope_base=10000.0, global_layout=mode == "global")
     O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     pos = pipe.pos_host.numpy()
     t = sample_rows(w, rank, pos[rank], 1024 // (w.B * w.H), outl)
