@@ -129,6 +129,7 @@ RANK_BWD_CASES = [
     (torch.bfloat16, 1, 2, 2048, 1, 128, True, "global"),
     (torch.bfloat16, 1, 2, 768, 4, 128, True, "global"),   # chunks of 96: tiles straddle chunks
     (torch.bfloat16, 2, 2, 320, 5, 64, True, "global"),    # chunks of 32, partial tiles
+    (torch.bfloat16, 1, 1, 4096, 64, 64, True, "global"),  # 64 ranks, one tile per chunk
     (torch.bfloat16, 1, 2, 1000, 4, 128, True, True),   # 250 rows per rank: ragged tiles
     (torch.bfloat16, 2, 3, 1000, 4, 64, True, True),
     (torch.float32, 1, 2, 64, 4, 16, True, False),      # the fp32 tiny shape

@@ -399,6 +399,7 @@ SHARE_CASES = [c for c in FUSED_CASES if (c[2] // c[3] // 2) % 32 == 0] + [
     (1, 2, 768, 4, 128, True),    # C = 96
     (2, 2, 320, 5, 64, True),     # C = 32, one 64-row workgroup per rank
     (1, 1, 1280, 4, 128, True),   # C = 160
+    (1, 1, 4096, 64, 64, True),   # 64 ranks: 64-block rings over 128 chunks of one tile each
 ]
 
 
