@@ -21,9 +21,10 @@
 //    through ds_read_b64_tr_b16.
 //  * Software pipeline: iteration t issues the matrix work of PV(t-1) and
 //    QK^T(t+1), then the exponentials of tile t, the row max of tile t+1 and
-//    the rare rescale.  The operand reads from LDS run six MFMAs ahead of
-//    their use; sched_group_barrier pins only that order of LDS reads and
-//    MFMAs (pinning the VALU work between the MFMAs as well measured slower).
+//    the rare rescale.  The operand reads from LDS run six (rank-major) or
+//    four (global layout) MFMAs ahead of their use; sched_group_barrier pins
+//    only that order of LDS reads and MFMAs (pinning the VALU work between the
+//    MFMAs as well measured slower).
 //  * K and V tiles of 32 keys live in two LDS buffers each.  Iteration t
 //    starts the copies of K(t+2) and V(t) straight from global memory into
 //    LDS (global_load_lds_dwordx4, no staging registers; offsets precomputed
@@ -34,13 +35,13 @@
 //    few per-lane bases plus an immediate offset, and no read has bank
 //    conflicts.  Each copy instruction writes 1 KiB of LDS contiguously.
 //  * Softmax rescaling is lazy and exact: the exponent reference is an integer
-//    (log2 units) raised only when a row's max grows by more than 2^32; the
+//    (log2 units) raised only when a row's max outgrows it by a factor 2^32; the
 //    rescale is then a power of two, applied with ldexp to O, l and the P of
 //    the tile already computed but not yet multiplied into O.  O is divided by
 //    the sum of the packed bf16 P (v_dot2_f32_bf16), i.e. exactly the weights
 //    the PV product used, so it stays a convex combination of V rows; lse uses
 //    the fp32 sum, which the bf16 rounding of a row's dominant weight would
-//    otherwise bias by up to 2^-9.
+//    otherwise bias by up to 2^-8 (relative).
 //  * Keys visible to a causal row form a prefix of the K block (positions
 //    increase), so the workgroup loops only over keys below the last row's
 //    bound and only tiles that cross a row's bound are masked per element.
