@@ -408,12 +408,9 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   const float c_log2 = scale * LOG2E;
 
   const int64_t Lrow = GL ? Lq * nblk : Lq;  // rows per head of every tensor (GL)
-  // Row of key u of this block / of query u of the rank, within a head.
+  // Row of key u of this block within a head.
   auto kmap = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
     return GL ? zig_row(blk, u, Lk, nblk) : u;
-  };
-  auto qmap = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
-    return GL ? zig_row(qrank, u, Lq, nblk) : u;
   };
   const __bf16* Kb = GL ? K + (int64_t)bh * Lrow * D : K + blk * kv_stride + (int64_t)bh * Lk * D;
   const __bf16* Vb = GL ? V + (int64_t)bh * Lrow * D : V + blk * kv_stride + (int64_t)bh * Lk * D;
@@ -459,11 +456,14 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   const f32x16 zero16 = {};
 
   // lse reference and delta of query tile t into LDS buffer b (first wave).
+  // A tile's rows are contiguous in either layout (GL: inside one chunk), so
+  // the row address is the chunk base plus the local row.
   auto stage_rows = [&](int t, int b) __attribute__((always_inline)) {
     if (tid < BN) {
       const int64_t q = (int64_t)t * BN + tid;
-      l2_lds[b][tid] = q < Lq ? lse_ref(lse_bh[qmap(q)]) : INFINITY;
-      dl_lds[b][tid] = q < Lq ? dl_bh[qmap(q)] : 0.f;
+      const int64_t base = (GL && (int64_t)t * BN >= Cq) ? q_hi_row : q_lo_row;
+      l2_lds[b][tid] = q < Lq ? lse_ref(lse_bh[base + q]) : INFINITY;
+      dl_lds[b][tid] = q < Lq ? dl_bh[base + q] : 0.f;
     }
   };
 
