@@ -318,6 +318,25 @@ cpa_status cpa_zigzag_permute_rope(const void *src, void *dst, cpa_dtype dt, int
                                    int32_t N, int32_t rank_lo, int32_t rank_hi, double base,
                                    int32_t pairing, void *stream);
 
+/*
+ * Check of the precondition on position tables (debug aid).  Under causal
+ * masking the attention calls take each block's positions as strictly
+ * increasing: with the zigzag
+ * layout a rank's positions are its two chunks in ascending order ("序列与
+ * 上下文并行", section 上下文并行：注意力本身切分, the Z-shaped assignment), and
+ * the kernels classify tiles, and find a row's visible keys, from that order.
+ * They do not check it; this call does, for `rows` tables of n positions each
+ * (a pos_all table is rows = N, n = L/N; a q_off / k_off table is rows = 1).
+ *   off        device int64 [rows, n]
+ *   first_bad  device int64 [1], written by the stream: the smallest flat
+ *              index i with i % n != 0 and off[i] <= off[i - 1], or rows * n
+ *              when every table is strictly increasing (also when it is empty)
+ * Two launches (a one-thread fill of first_bad, then the check), no memset;
+ * the caller reads first_bad after synchronising the stream.
+ */
+cpa_status cpa_check_offsets(const int64_t *off, int64_t rows, int64_t n, int64_t *first_bad,
+                             void *stream);
+
 /* Text of the last error on the calling thread ("" if none); valid until the
  * thread's next call into the library. */
 const char *cpa_last_error(void);

@@ -98,6 +98,27 @@ def contiguous_layout(L: int, N: int) -> np.ndarray:
     return np.arange(L, dtype=np.int64).reshape(N, L // N)
 
 
+def first_non_increasing(pos) -> int | None:
+    """Flat index of the first entry of a position table ([n] or [rows, n])
+    that is not the first of its row and does not exceed the entry before it;
+    None if every row is strictly increasing.
+
+    Within a rank the Z-shaped assignment gives its early chunk, then its late
+    chunk, each in ascending order ("序列与上下文并行", 上下文并行), so every
+    row of a zigzag table increases; causal masking by position relies on
+    that order.  A plain scan of the rows.
+    """
+    a = np.asarray(pos, dtype=np.int64)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    rows, n = a.shape
+    for r in range(rows):
+        for t in range(1, n):
+            if a[r, t] <= a[r, t - 1]:
+                return r * n + t
+    return None
+
+
 def causal_pairs(q_pos: np.ndarray, k_pos: np.ndarray) -> int:
     """Number of (query, key) pairs with key position <= query position."""
     k_sorted = np.sort(np.asarray(k_pos))

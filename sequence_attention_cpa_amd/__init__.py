@@ -7,6 +7,7 @@ tensors' device.  Nothing is computed here: every call goes to the library.
 from __future__ import annotations
 
 import ctypes
+import os
 
 from ._lib import (CPA_BF16, CPA_EDTYPE, CPA_EINVAL, CPA_ESHAPE, CPA_F32,  # noqa: F401
                    CPA_ROPE_HALF, CPA_ROPE_INTERLEAVED, CpaError, check, last_error, load,
@@ -14,8 +15,8 @@ from ._lib import (CPA_BF16, CPA_EDTYPE, CPA_EINVAL, CPA_ESHAPE, CPA_F32,  # noq
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
            "rank_forward_fused", "share_forward", "share_backward", "zigzag_permute", "rope",
-           "zigzag_permute_rope", "backward_delta", "partial_backward", "rank_backward", "last_error",
-           "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
+           "zigzag_permute_rope", "backward_delta", "partial_backward", "rank_backward",
+           "check_offsets", "debug_offsets", "last_error", "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
 
 
 def _torch():
@@ -62,6 +63,52 @@ def _need_gpu(*ts):
             raise CpaError(CPA_EINVAL, "tensors must be contiguous")
 
 
+_debug_offsets = os.environ.get("CPA_DEBUG_OFFSETS", "0") not in ("", "0")
+
+
+def debug_offsets(enable: bool) -> None:
+    """Switch the offsets check on or off for every later causal call.
+
+    When on, each call with causal masking first runs check_offsets on its
+    position tables and raises CpaError(CPA_EINVAL) naming the first entry
+    that does not exceed its predecessor.  The check synchronises the stream
+    (it reads the answer back), so it is a debugging aid: off by default, on
+    from the start when the environment sets CPA_DEBUG_OFFSETS=1."""
+    global _debug_offsets
+    _debug_offsets = bool(enable)
+
+
+def check_offsets(off):
+    """Flat index of the first entry of `off` (int64 on the GPU, [n] or
+    [rows, n]) that is not the first of its row and does not exceed the entry
+    before it; None if every row is strictly increasing.  Synchronises the
+    stream to read the answer."""
+    torch = _torch()
+    if off.dim() == 1:
+        rows, n = 1, off.shape[0]
+    elif off.dim() == 2:
+        rows, n = off.shape
+    else:
+        raise CpaError(CPA_ESHAPE, f"off must be [n] or [rows, n], got shape {tuple(off.shape)}")
+    _expect(off, off.shape, (torch.int64,), "off")
+    _need_gpu(off)
+    first_bad = torch.empty(1, dtype=torch.int64, device=off.device)
+    check(load().cpa_check_offsets(_ptr(off), rows, n, _ptr(first_bad), _stream(off)))
+    i = int(first_bad.item())
+    return None if i == rows * n else i
+
+
+def _debug_check(causal, **tables):
+    if not (_debug_offsets and causal):
+        return
+    for name, t in tables.items():
+        i = check_offsets(t)
+        if i is not None:
+            n = t.shape[-1]
+            raise CpaError(CPA_EINVAL, f"{name} is not strictly increasing: row {i // n}, entry "
+                                       f"{i % n} does not exceed the entry before it")
+
+
 def zigzag_layout(L: int, N: int):
     """int64 CPU tensor [N, L/N] of global token positions per rank (host call)."""
     torch = _torch()
@@ -90,6 +137,7 @@ def partial(Q, K, V, q_off, k_off, causal: bool, scale: float = 0.0, out=None, l
     _expect(out, (B, H, Lq, D), f32, "out")
     _expect(lse, (B, H, Lq), f32, "lse")
     _need_gpu(Q, K, V, q_off, k_off, out, lse)
+    _debug_check(causal, q_off=q_off, k_off=k_off)
     check(load().cpa_partial(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, Lq, Lk, D,
                              _ptr(q_off), _ptr(k_off), int(bool(causal)), float(scale),
                              _ptr(out), _ptr(lse), _stream(Q)))
@@ -144,6 +192,7 @@ def rank_forward(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool, scale
     if workspace is not None and workspace.dtype != torch.uint8:
         raise CpaError(CPA_EDTYPE, f"workspace has dtype {workspace.dtype}, expected torch.uint8")
     _need_gpu(Q_i, K_all, V_all, pos_all, out, lse, workspace)
+    _debug_check(causal, pos_all=pos_all)
     check(load().cpa_rank_forward(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                   _dtype_code(Q_i), B, H, L, D, int(bool(causal)), float(scale),
                                   _ptr(out), _ptr(lse), _ptr(workspace),
@@ -162,6 +211,7 @@ def rank_forward_fused(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
         lse = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
     _check_rank_major(Q_i, K_all, V_all, pos_all, N, out, lse)
     _need_gpu(Q_i, K_all, V_all, pos_all, out, lse)
+    _debug_check(causal, pos_all=pos_all)
     check(load().cpa_rank_forward_fused(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                         _dtype_code(Q_i), B, H, Lr * N, D, int(bool(causal)),
                                         float(scale), _ptr(out), _ptr(lse), _stream(Q_i)))
@@ -187,6 +237,7 @@ def share_forward(Q, K, V, pos_all, N: int, causal: bool, scale: float = 0.0, ra
     _expect(out, (B, H, L, D), f32, "out")
     _expect(lse, (B, H, L), f32, "lse")
     _need_gpu(Q, K, V, pos_all, out, lse)
+    _debug_check(causal, pos_all=pos_all)
     check(load().cpa_share_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _dtype_code(Q), B, H,
                                    L, D, N, rank_lo, rank_hi, int(bool(causal)), float(scale),
                                    _ptr(out), _ptr(lse), _stream(Q)))
@@ -216,6 +267,7 @@ def share_backward(Q, K, V, pos_all, O, dO, lse, N: int, causal: bool, dK, dV,
     _expect(delta, (B, H, L), f32, "delta")
     _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _need_gpu(Q, K, V, pos_all, O, dO, lse, dK, dV, dQ, delta)
+    _debug_check(causal, pos_all=pos_all)
     check(load().cpa_share_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _ptr(O), _ptr(dO),
                                     _ptr(lse), _dtype_code(Q), B, H, L, D, N, rank_lo, rank_hi,
                                     int(bool(causal)), float(scale), _ptr(dQ), _ptr(dK), _ptr(dV),
@@ -326,6 +378,7 @@ def partial_backward(Q, K, V, dO, lse, delta, q_off, k_off, causal: bool, dQ, dK
     _expect(dK, (B, H, Lk, D), f32, "dK")
     _expect(dV, (B, H, Lk, D), f32, "dV")
     _need_gpu(Q, K, V, dO, lse, delta, q_off, k_off, dQ, dK, dV)
+    _debug_check(causal, q_off=q_off, k_off=k_off)
     check(load().cpa_partial_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(lse), _ptr(delta),
                                       _dtype_code(Q), B, H, Lq, Lk, D, _ptr(q_off), _ptr(k_off),
                                       int(bool(causal)), float(scale), _ptr(dQ), _ptr(dK),
@@ -351,6 +404,7 @@ def rank_backward(i: int, N: int, Q_i, K_all, V_all, pos_all, O_i, dO_i, lse_i, 
     _expect(dQ, (B, H, Lr, D), f32, "dQ")
     _expect(delta, (B, H, Lr), f32, "delta")
     _need_gpu(Q_i, K_all, V_all, pos_all, O_i, dO_i, lse_i, dK_all, dV_all, dQ, delta)
+    _debug_check(causal, pos_all=pos_all)
     check(load().cpa_rank_backward(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all), _ptr(pos_all),
                                    _ptr(O_i), _ptr(dO_i), _ptr(lse_i), _dtype_code(Q_i), B, H,
                                    Lr * N, D, int(bool(causal)), float(scale), _ptr(dQ),

@@ -51,6 +51,7 @@ SIGNATURES = {
                                 _vp]),
     "cpa_zigzag_permute_rope": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32, _vp,
                                                _i32, _i32, _i32, _f64, _i32, _vp]),
+    "cpa_check_offsets": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "cpa_last_error": (ctypes.c_char_p, []),
     "cpa_version": (ctypes.c_char_p, []),
 }

@@ -52,6 +52,11 @@ hipError_t launch_permute(const void* src, void* dst, int64_t row_bytes, int64_t
                           const int64_t* pos_all, int N, int rank_lo, int rank_hi, bool inverse,
                           hipStream_t stream);
 
+// first_bad <- smallest i with i % n != 0 and off[i] <= off[i - 1] over
+// `rows` tables of n positions, or rows * n if there is none.
+hipError_t launch_check_offsets(const int64_t* off, int64_t rows, int64_t n, int64_t* first_bad,
+                                hipStream_t stream);
+
 // Rotary position embedding of rows at given global positions (D % 8 == 0).
 // Index space: nr x Lr positions pos[rr*Lr + t]; destination rows
 // (rr*BH + bh)*Lr + t of [nr, BH, Lr, D]; source rows bh*L + p of global

@@ -277,6 +277,20 @@ cpa_status cpa_zigzag_permute(const void* src, void* dst, int32_t elem_bytes, in
                   "permute launch");
 }
 
+cpa_status cpa_check_offsets(const int64_t* off, int64_t rows, int64_t n, int64_t* first_bad,
+                             void* stream) {
+  if (rows < 0 || n < 0) return fail(CPA_ESHAPE, "rows and n must be >= 0 (rows=%lld, n=%lld)",
+                                     (long long)rows, (long long)n);
+  if (n > 0 && rows > ((int64_t)1 << 62) / n)
+    return fail(CPA_ESHAPE, "rows * n is limited to 2^62 entries");
+  if (!first_bad) return fail(CPA_EINVAL, "null first_bad");
+  if (rows * n > 0 && !off) return fail(CPA_EINVAL, "null offset table");
+  if (!aligned(off, 8) || !aligned(first_bad, 8))
+    return fail(CPA_EINVAL, "off and first_bad must be 8-byte aligned");
+  return from_hip(cpa::launch_check_offsets(off, rows, n, first_bad, (hipStream_t)stream),
+                  "offsets check launch");
+}
+
 cpa_status cpa_rope(const void* x, void* y, cpa_dtype dt, int32_t B, int32_t H, int64_t rows,
                     int32_t D, const int64_t* pos, double base, int32_t pairing, void* stream) {
   cpa_status st = check_rope(dt, B, H, D, base, pairing);

@@ -7,6 +7,9 @@
 //  * permute: gather/scatter of whole rows between the global token order
 //    and the rank-major zigzag order (same page, section 工程实践: the data
 //    of each rank follows the CP layout).
+//  * offsets check: finds the first entry of a position table that does not
+//    exceed its predecessor; the attention kernels assume strictly
+//    increasing positions within every block.
 #include "cpa_internal.h"
 
 #include <cmath>
@@ -157,6 +160,25 @@ __global__ __launch_bounds__(256) void permute_kernel(const W* __restrict__ src,
   }
 }
 
+// first_bad <- rows * n: the "every table increases" answer that the check
+// lowers with an atomic minimum (a fill kernel, not a memset, so that the
+// pair can be captured in a graph).
+__global__ void offsets_init_kernel(unsigned long long* first_bad, int64_t total) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *first_bad = (unsigned long long)total;
+}
+
+// Entry i of `rows` tables of n positions is bad if it is not the first of
+// its table and does not exceed entry i - 1.
+__global__ __launch_bounds__(256) void offsets_check_kernel(const int64_t* __restrict__ off,
+                                                            int64_t rows, int64_t n,
+                                                            unsigned long long* first_bad) {
+  const int64_t total = rows * n;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    if (i % n != 0 && off[i] <= off[i - 1]) atomicMin(first_bad, (unsigned long long)i);
+  }
+}
+
 unsigned grid_for(int64_t n, int per_block) {
   int64_t b = (n + per_block - 1) / per_block;
   const int64_t cap = 256 * 8 * 8;  // 8 resident blocks per CU is enough to saturate HBM
@@ -221,6 +243,17 @@ hipError_t launch_permute(const void* src, void* dst, int64_t row_bytes, int64_t
                        (const uint32_t*)src, (uint32_t*)dst, words, BH, L, Lr, pos_all, rank_lo, nr,
                        inv);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_check_offsets(const int64_t* off, int64_t rows, int64_t n, int64_t* first_bad,
+                                hipStream_t stream) {
+  unsigned long long* fb = reinterpret_cast<unsigned long long*>(first_bad);
+  hipLaunchKernelGGL(offsets_init_kernel, dim3(1), dim3(64), 0, stream, fb, rows * n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows * n == 0) return e;
+  hipLaunchKernelGGL(offsets_check_kernel, dim3(grid_for(rows * n, 256)), dim3(256), 0, stream,
+                     off, rows, n, fb);
   return hipGetLastError();
 }
 

@@ -254,6 +254,50 @@ def test_rope_rejects(lib, kw, status):
     assert cpa.last_error() != ""
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(off=None), _lib.CPA_EINVAL),
+    (dict(first_bad=None), _lib.CPA_EINVAL),
+    (dict(off=P + 4), _lib.CPA_EINVAL),
+    (dict(first_bad=P + 12), _lib.CPA_EINVAL),
+    (dict(rows=-1), _lib.CPA_ESHAPE),
+    (dict(n=-5), _lib.CPA_ESHAPE),
+    (dict(rows=1 << 40, n=1 << 23), _lib.CPA_ESHAPE),
+])
+def test_check_offsets_rejects(lib, kw, status):
+    a = dict(off=P, rows=4, n=64, first_bad=P + 8192)
+    a.update(kw)
+    assert lib.cpa_check_offsets(a["off"], a["rows"], a["n"], a["first_bad"], None) == status
+    assert cpa.last_error()
+
+
+def test_debug_offsets_switch(monkeypatch):
+    """The binding's offsets check runs only when the switch is on and the
+    call is causal, and names the table and entry of the first break."""
+    seen = []
+    monkeypatch.setattr(cpa, "check_offsets", lambda t: seen.append(t) or t.answer)
+
+    class Table:
+        shape = (4, 10)
+        answer = None
+
+    bad = Table()
+    bad.answer = 23
+    cpa.debug_offsets(False)
+    cpa._debug_check(True, q_off=bad)
+    cpa.debug_offsets(True)
+    try:
+        cpa._debug_check(False, q_off=bad)
+        assert seen == []
+        cpa._debug_check(True, q_off=Table(), k_off=Table())
+        assert len(seen) == 2
+        with pytest.raises(cpa.CpaError) as e:
+            cpa._debug_check(True, pos_all=bad)
+        assert e.value.status == _lib.CPA_EINVAL and "pos_all" in str(e.value)
+        assert "row 2, entry 3" in str(e.value)
+    finally:
+        cpa.debug_offsets(False)
+
+
 def test_rope_zero_rows_is_a_no_op(lib):
     assert _rope(lib, rows=0, x=None, y=None, pos=None) == _lib.CPA_OK
 

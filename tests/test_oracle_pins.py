@@ -415,13 +415,38 @@ def check_backward_invariants(orc):
     assert np.max(np.abs(dQ)) < 1e-12 and np.max(np.abs(dK)) < 1e-12
 
 
+def check_first_non_increasing(orc):
+    """Hand-checked tables: equal neighbours break strict increase, a row may
+    restart below the previous row's end, one-entry and empty rows pass, and
+    the answer is the smallest flat index; the zigzag tables of the workloads
+    increase within every rank; and on small random tables the answer is the
+    first True of the row-wise difference test, found by np.nonzero."""
+    f = orc.first_non_increasing
+    assert f([0, 1, 2, 9]) is None
+    assert f([0, 1, 1, 2]) == 2
+    assert f([5, 4, 3]) == 1
+    assert f([[0, 7], [1, 8]]) is None
+    assert f([[0, 7], [8, 8]]) == 3
+    assert f([[3], [2], [1]]) is None
+    assert f(np.zeros((0,), np.int64)) is None
+    assert f([[0, 2, 1, 0], [0, 1, 2, 3]]) == 2
+    assert f([[0, 1, 2, 3], [9, 8, 10, 11]]) == 5
+    for L, N in [(64, 4), (12288, 4), (131072, 4)]:
+        assert f(orc.zigzag_layout(L, N)) is None
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        a = rng.integers(0, 6, size=(3, 5))
+        r, c = np.nonzero(np.diff(a, axis=1) <= 0)
+        assert f(a) == (None if len(r) == 0 else int(r[0] * 5 + c[0] + 1))
+
+
 PINS = [check_layout_golden, check_layout_permutation, check_layout_balance, check_ring_order,
         check_permute, check_brute_force, check_sdpa, check_uniform_scores,
         check_constant_v_and_first_row, check_chunk_merge_invariant, check_partial_empty_rows,
         check_merge_algebra, check_structural, check_sampled_rows, check_rope_sinusoid_table,
         check_rope_norm_and_identity, check_rope_relative, check_rope_global_positions,
         check_backward_autograd, check_backward_finite_differences,
-        check_backward_ring_decomposition, check_backward_invariants]
+        check_backward_ring_decomposition, check_backward_invariants, check_first_non_increasing]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -486,6 +511,9 @@ MUTANTS = {
     "bwd ring block": ("dK[j] += dk", "dK[i] += dk"),
     "bwd causal key range": ("kend = (int(q_pos[a:b].max()) + 1) if causal",
                              "kend = (int(q_pos[a:b].max())) if causal"),
+    "offsets not strict": ("if a[r, t] <= a[r, t - 1]:", "if a[r, t] < a[r, t - 1]:"),
+    "offsets across rows": ("for t in range(1, n):", "for t in range(n):"),
+    "offsets flat index": ("return r * n + t", "return r * n + t - 1"),
     "rope position offset": ("phi = np.asarray(pos, dtype=np.float64)[:, None]",
                              "phi = (np.asarray(pos, dtype=np.float64)[:, None] + 1)"),
 }
