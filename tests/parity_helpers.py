@@ -77,12 +77,16 @@ def check_empty_rows(O, lse, O_ref, lse_ref):
     return ~neg
 
 
-def assert_bf16_close(O, lse, O_ref, lse_ref, what=""):
+def assert_bf16_close(O, lse, O_ref, lse_ref, what="", v_scale=1.0):
+    """v_scale: how much larger than unit scale V's largest rows are.  O is a
+    convex combination of V rows, so the error that bf16 weights leave in it
+    scales with them; the O bounds are the unit-scale ones times v_scale."""
     fin = check_empty_rows(O, lse, O_ref, lse_ref)
     d = np.abs(O - O_ref)
     mx, mean = float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
-    assert mx <= BF16_MAX_ABS, f"{what}: max |dO| {mx:.3e} > {BF16_MAX_ABS}"
-    assert mean <= BF16_MEAN_ABS, f"{what}: mean |dO| {mean:.3e} > {BF16_MEAN_ABS}"
+    mx_tol, mean_tol = BF16_MAX_ABS * v_scale, BF16_MEAN_ABS * v_scale
+    assert mx <= mx_tol, f"{what}: max |dO| {mx:.3e} > {mx_tol}"
+    assert mean <= mean_tol, f"{what}: mean |dO| {mean:.3e} > {mean_tol}"
     dl = np.abs(lse[fin] - lse_ref[fin])
     bound = LSE_REL * np.maximum(1.0, np.abs(lse_ref[fin]))
     assert np.all(dl <= bound), f"{what}: lse off by {float((dl / bound).max()):.2f}x tolerance"
