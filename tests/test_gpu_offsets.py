@@ -116,3 +116,46 @@ def test_debug_mode_rejects_bad_tables_before_causal_calls():
         torch.cuda.synchronize()
     finally:
         cpa.debug_offsets(False)
+
+
+def test_debug_mode_covers_the_ring_and_backward_calls():
+    """The rank-major ring, the partial backward, the ring backward and the
+    global-layout backward also refuse a bad table before launching."""
+    g = torch.Generator().manual_seed(12)
+    B, H, L, D, N = 1, 1, 256, 64, 2
+    Lr = L // N
+    bf = dict(dtype=torch.bfloat16)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    Q, K, V, dO = (torch.randn((B, H, L, D), generator=g).to(**bf).to(DEV) for _ in range(4))
+    Kr, Vr = (torch.randn((N, B, H, Lr, D), generator=g).to(**bf).to(DEV) for _ in range(2))
+    Qi, dOi = (torch.randn((B, H, Lr, D), generator=g).to(**bf).to(DEV) for _ in range(2))
+    pos = torch.from_numpy(cpa_oracle.zigzag_layout(L, N)).to(DEV)
+    bad_pos = pos.clone()
+    bad_pos[0, 3] = bad_pos[0, 2]
+    bad_off = torch.arange(Lr, dtype=torch.int64, device=DEV)
+    bad_off[5] = bad_off[4]
+    good_off = torch.arange(Lr, dtype=torch.int64, device=DEV)
+    O, lse = torch.zeros((B, H, L, D), **f32), torch.zeros((B, H, L), **f32)
+    Oi, lsei = torch.zeros((B, H, Lr, D), **f32), torch.zeros((B, H, Lr), **f32)
+    dK, dV, dQ = (torch.zeros((B, H, L, D), **f32) for _ in range(3))
+    dKr, dVr = torch.zeros((N, B, H, Lr, D), **f32), torch.zeros((N, B, H, Lr, D), **f32)
+    dQi, dKi, dVi = (torch.zeros((B, H, Lr, D), **f32) for _ in range(3))
+    calls = {
+        "rank_forward_fused": lambda: cpa.rank_forward_fused(0, N, Qi, Kr, Vr, bad_pos, True),
+        "partial_backward": lambda: cpa.partial_backward(Qi, Qi, Qi, dOi, lsei, lsei, good_off,
+                                                         bad_off, True, dQi, dKi, dVi),
+        "rank_backward": lambda: cpa.rank_backward(0, N, Qi, Kr, Vr, bad_pos, Oi, dOi, lsei, True,
+                                                   dKr, dVr),
+        "share_backward": lambda: cpa.share_backward(Q, K, V, bad_pos, O, dO, lse, N, True, dK,
+                                                     dV, dQ=dQ),
+    }
+    cpa.debug_offsets(True)
+    try:
+        for name, call in calls.items():
+            with pytest.raises(cpa.CpaError) as e:
+                call()
+            assert e.value.status == cpa.CPA_EINVAL, name
+            say(f"debug offsets, {name}: {e.value}")
+        torch.cuda.synchronize()
+    finally:
+        cpa.debug_offsets(False)
