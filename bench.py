@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0
 PMC_FILES = {"global": os.path.join(ROOT, "profiles", "ring_global_128k_pmc.json"),
              "fused": os.path.join(ROOT, "profiles", "ring_fused_128k_pmc.json"),
              "partials": os.path.join(ROOT, "profiles", "partial_attn_128k_pmc.json")}
-KERNEL_SRC = os.path.join(ROOT, "sequence_attention_cpa_amd", "csrc", "partial_attn.hip")
+KERNEL_SRC = os.path.join(ROOT, "sequence_attention_cpa_amd", "csrc", "attn_fwd.hip")
 
 
 def causal_pairs(q_pos, k_pos):
@@ -294,16 +294,16 @@ def main():
         return {"median": round(float(np.median(x)), 4), "min": round(float(np.min(x)), 4),
                 "p90": round(float(np.percentile(x, 90)), 4)}
     if args.ring == "global":
-        dom_kernel = (f"partial_attn_mfma_kernel<{w.D}, global layout> (one launch, {w.N} K/V "
+        dom_kernel = (f"attn_fwd_kernel<{w.D}, global layout> (one launch, {w.N} K/V "
                       "blocks)")
         dom_ms = float(g_ms.mean())
         dom_flop = useful
     elif fused:
-        dom_kernel = f"partial_attn_mfma_kernel<{w.D}> (one launch, {w.N} K/V blocks)"
+        dom_kernel = f"attn_fwd_kernel<{w.D}> (one launch, {w.N} K/V blocks)"
         dom_ms = float(f_ms.mean())
         dom_flop = useful
     else:
-        dom_kernel = f"partial_attn_mfma_kernel<{w.D}> (one K/V block)"
+        dom_kernel = f"attn_fwd_kernel<{w.D}> (one K/V block)"
         dom_ms = p_avg_ms
         dom_flop = float(p_flops.mean())
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcpattn.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["cpattn.cpp", "partial_attn.hip", "rowwise_merge_permute.hip", "rope.hip",
+SOURCES = ["cpattn.cpp", "attn_fwd.hip", "rowwise_merge_permute.hip", "rope.hip",
            "attn_backward.hip"]
 ARCH = "gfx950"
 FLAGS = [

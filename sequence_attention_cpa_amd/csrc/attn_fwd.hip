@@ -1,0 +1,624 @@
+// Partial attention of the ring on CDNA4 (gfx950) matrix cores: a rank's
+// queries against one or more K/V blocks, returning (O, lse) so that other
+// blocks can be folded in by online softmax ("序列与上下文并行", section
+// 上下文并行：注意力本身切分).  Scores are Q K^T * scale, hidden keys get -inf,
+// softmax over keys, weights times V ("Tensor并行与算子拆分", section
+// 注意力的并行化优化).  Causal visibility compares global token positions
+// (same page as the ring, section 工程实践: every rank knows its global offsets).
+//
+// Design (bf16, D = 64 or 128):
+//  * One workgroup = 8 waves = 256 query rows (32 per wave), one workgroup
+//    per CU, two waves per SIMD.  Each K/V tile a workgroup stages in LDS
+//    serves all 256 rows, which halves the L2-to-LDS traffic of four-wave
+//    workgroups; at this density the part is power-limited, and bytes moved
+//    cost clock.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: K (32 keys x 16 d) is the A operand read from
+//    LDS, the wave's Q rows are the B operand held in registers for the whole
+//    kernel.  A lane then holds 16 keys of ONE query.  O is accumulated
+//    transposed, O^T += V^T P^T: P (round to nearest even bf16) is the B
+//    operand straight from registers, V^T comes from row-major V in LDS
+//    through ds_read_b64_tr_b16.
+//  * The steady loop is ONE basic block per 32-key tile: the copies of later
+//    K/V tiles (branch-free: past the last full tile they re-copy it into a
+//    free buffer), the 16 MFMAs of PV(t-1) and QK^T(t+1), and the softmax of
+//    tile t, so the scheduler can hide the softmax arithmetic between the
+//    matrix instructions.  Only the overflow check below branches, at the
+//    end of the block, to a slow path that is taken a few times per row.
+//  * No per-tile row max.  The exponent reference m is an integer (log2
+//    units) fixed by the first tile a row sees; every later tile computes
+//    P = 2^(s*c - m) directly and checks its fp32 sum.  A sum above 2^40
+//    means some score outgrew the reference by more than 2^36: the slow path
+//    then takes the tile's real max, raises m to its ceiling, rescales O and
+//    the sums by the exact power of two and redoes the tile.  P stays below
+//    2^40, so bf16 P and the fp32 accumulators cannot overflow.
+//  * O is divided by the sum of the bf16-rounded P (the weights the PV
+//    product used), so it stays a convex combination of V rows; lse uses the
+//    fp32 sum of the unrounded P.  The bf16 sum comes from the matrix core:
+//    two more MFMAs per tile multiply a row of ones into the same P operand,
+//    which costs less than unpacking and adding the bf16 pairs on the VALU
+//    (and the dot-product instructions stall the matrix pipe).
+//  * K and V tiles live in four LDS buffers each; K(t+3) and V(t+2) are
+//    copied during iteration t straight from global memory into LDS
+//    (global_load_lds_dwordx4), and each iteration waits only for the copies
+//    of the iteration before, so a copy has two iterations to land.
+//  * Tiles are classified per wave from the block's key positions: tiles
+//    every row of the wave fully sees (the steady loop, which every wave of
+//    the workgroup runs up to the first wave's count), and the few that cross
+//    a row's causal bound or the block end (a simple, non-pipelined tail with
+//    an element mask and an exact row max).  Keys visible to a causal row are
+//    a prefix of the block (positions increase).  Rows that see no key write
+//    O = 0, lse = -inf.
+//  * Global layout (cpa_share_forward): Q, K, V, O, lse are the whole sequence
+//    in token order and rank r's local row u is global row zig(r, u) (chunk r
+//    for u < C, chunk 2N-1-r after, C = L/(2N)); the positions are that same
+//    closed form, so no position table is read.
+//  * Workgroups are issued longest-first (last query tiles first), heads
+//    fastest, so each XCD keeps working on the same heads' K/V in its L2.
+#include "cpa_internal.h"
+#include "mfma_tile.h"
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+namespace cpa {
+namespace {
+
+using namespace tile;
+
+// Waves per workgroup (32 query rows each); the K/V tiles a workgroup stages
+// in LDS serve all of them.
+constexpr int WAVES = 8;
+constexpr int BM = 32 * WAVES;       // query rows per workgroup
+constexpr int NTHREADS = 64 * WAVES;
+static_assert(NTHREADS * cpa::kMfmaRows == BM * cpa::kMfmaThreads,
+              "the host checks launch sizes with two threads per query row");
+constexpr int NBUF = 4;     // LDS buffers per operand
+constexpr int K_AHEAD = 3;  // iteration t copies K(t + K_AHEAD); at most NBUF
+constexpr int V_AHEAD = 2;  // iteration t copies V(t + V_AHEAD); at most NBUF - 2
+static_assert(K_AHEAD <= NBUF && V_AHEAD <= NBUF - 2, "copy would overwrite a tile in use");
+// Operand reads in flight ahead of the MFMA that uses them (2 to 6 measured
+// within 1.5 %).
+constexpr int FWD_PF = 3;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+// A lane's 16 weights of a tile summing above this send the wave to the slow
+// path (some weight exceeds 2^36).
+constexpr float TILE_SUM_MAX = 0x1p40f;
+// Reference before a row's first tile: any finite score overflows against it.
+constexpr float M_INIT = -0x1p100f;
+
+// LDS layout of a 32-row K or V tile, in 16-byte slots, with column blocks
+// of W chunks (W = 4: 64-byte blocks, W = 8: 128-byte blocks): logical chunk
+// c of row r sits at slot 32W*(c/W) + W*r + ((c%W) ^ key(r)).  Column blocks
+// keep every operand read at one of a few per-lane bases plus a compile-time
+// offset; the XOR key spreads each 16-lane phase of the K reads and each
+// 32-lane half of the transposing V reads over distinct banks.  Copy
+// instruction n fills slots [64n, 64n + 64): 16 rows x 64 bytes of the tile
+// (W = 4) or 8 rows x 128 bytes, whole cache lines (W = 8).
+template <int W>
+__device__ __forceinline__ int lds_key(int r) {
+  if constexpr (W == 4) return (r >> 2) & 3;
+  else return (((r >> 1) & 1) ? 5 : 0) ^ (((r >> 2) & 1) ? 2 : 0) ^ (((r >> 3) & 1) ? 4 : 0);
+}
+template <int W>
+__device__ __forceinline__ int lds_slot(int r, int c) {
+  return 32 * W * (c / W) + W * r + ((c % W) ^ lds_key<W>(r));
+}
+
+// Number of keys of a zigzag block (rank b's rows: chunk b, then chunk
+// 2N-1-b, C rows each) at positions <= x.
+__device__ __forceinline__ int64_t zig_count_le(int b, int nblk, int64_t C, int64_t x) {
+  const int64_t lo = x - (int64_t)b * C + 1;
+  const int64_t hi = x - (int64_t)(2 * nblk - 1 - b) * C + 1;
+  return (lo < 0 ? 0 : (lo > C ? C : lo)) + (hi < 0 ? 0 : (hi > C ? C : hi));
+}
+
+// Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
+// K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
+// the order b = first + 1, first + 2, ..., first (mod nblk).  One block is one
+// ring step (cpa_partial); nblk = N with first = i is rank i's whole ring, the
+// running (O, reference, sums) staying in registers from one block to the
+// next.  The rank's own block comes last: in every other block a query tile
+// sees either none of the keys or the same whole prefix as its neighbours,
+// so the workgroups of a head sweep those blocks in step and share each K/V
+// tile through L2.
+//
+// GL (global layout): Q, K, V, O and lse are [BH, N * Lq, ...] in global
+// token order; rank r's local row u is global row zig(r, u), which is also
+// its position.  Lq/2 is a multiple of 32, so every 32-row tile is
+// contiguous in memory and lies in one chunk.
+template <int D, bool GL, int W>
+__global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ O,
+    float* __restrict__ lse, int BH, int Lq, int Lk, int64_t kv_stride, int64_t koff_stride,
+    int nblk, int first, int causal, float c_log2, int n_qtiles) {
+  using G = Geo<D>;
+  constexpr int TB = G::TILE_BYTES;
+  constexpr int RB = G::ROW_BYTES;
+  constexpr int KK = G::KK;
+  constexpr int DB = G::DB;
+  constexpr int NCP = TB / 1024;  // 1 KiB copy instructions per tile
+  constexpr int IPW = NCP / WAVES > 0 ? NCP / WAVES : 1;  // ... per wave (extra waves repeat)
+  constexpr int KB = W / 2;     // K operand base registers
+  constexpr int BLK = 512 * W;  // bytes per column block of a tile
+  __shared__ __attribute__((aligned(1024))) char k_lds_raw[NBUF * TB];
+  __shared__ __attribute__((aligned(1024))) char v_lds_raw[NBUF * TB];
+  lds_char* const Kl = (lds_char*)k_lds_raw;
+  lds_char* const Vl = (lds_char*)v_lds_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const int lr = lane & 31;
+  const int bh = blockIdx.x % BH;
+  const int qt = n_qtiles - 1 - blockIdx.x / BH;
+  const int q0 = qt * BM;                         // first local row of the workgroup
+  const int qlast = min(q0 + BM, Lq) - 1;         // its last valid row
+  const int w0 = q0 + wv * 32;                    // first local row of this wave
+  const int qrow = w0 + lr;
+  const int qrow_c = qrow < Lq ? qrow : Lq - 1;
+
+  const int64_t C = Lq / 2;                     // chunk length (GL)
+  const int64_t Lrow = GL ? (int64_t)Lq * nblk : Lq;  // rows per head in Q / O / lse
+  // global row of rank r's local row u (GL)
+  auto zig = [&](int r, int64_t u) __attribute__((always_inline)) -> int64_t {
+    const bool lo = u < C;
+    return (lo ? r : 2 * nblk - 1 - r) * C + (lo ? u : u - C);
+  };
+  auto qpos = [&](int u) __attribute__((always_inline)) -> int64_t {
+    return GL ? zig(first, u) : q_off[u];
+  };
+  const __bf16* Qbh = Q + (int64_t)bh * Lrow * D;
+  float* Obh = O + (int64_t)bh * Lrow * D;
+  float* lse_bh = lse + (int64_t)bh * Lrow;
+  // Positions of the workgroup's first and last rows and of this wave's
+  // (waves past Lq take the last row: they compute nothing that is stored).
+  const int wfirst = w0 < Lq ? w0 : Lq - 1;
+  const int wlast = (w0 + 31 < Lq ? w0 + 31 : Lq - 1);
+  int64_t pq_g0 = 0, pq_gl = 0, pq_w0 = 0, pq_wl = 0, my_qpos = 0;
+  if (causal) {
+    pq_g0 = qpos(q0);
+    pq_gl = qpos(qlast);
+    pq_w0 = qpos(wfirst);
+    pq_wl = qpos(wlast);
+    my_qpos = qpos(qrow_c);
+  }
+
+  // ---- per-lane constants -------------------------------------------------
+  // Q rows of this wave as the B operand: lane holds Q[qrow][kk*16 + hi*8 .. +7].
+  bf16x8 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(Qbh + (GL ? zig(first, qrow_c) : qrow_c) * D +
+                                              kk * 16 + hi * 8);
+  // K operand of kk: tile row lr, logical chunk kk*2 + hi, at byte
+  // (kk / KB) * BLK + kbase[kk % KB] of the tile.
+  int kbase[KB];
+#pragma unroll
+  for (int e = 0; e < KB; ++e) kbase[e] = lds_slot<W>(lr, e * 2 + hi) * 16;
+  // V operand of (half, db): two transposing reads (p = 0, 1) of rows
+  // half*16 + vrow + 8p, 8 bytes inside chunk db*4 + vch, at byte
+  // vaddr(half, db, p) of the tile.
+  const int vrow = hi * 4 + ((lane & 15) >> 2);
+  const int vch = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+  const int vsub = (lane & 1) * 8;
+  int vbase[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    vbase[e] = (W == 4 ? lds_slot<W>(vrow + 8 * e, vch) : lds_slot<W>(vrow, 4 * e + vch)) * 16 +
+               vsub;
+  auto vaddr = [&](int half, int db, int p) __attribute__((always_inline)) -> int {
+    if constexpr (W == 4) return half * 1024 + db * 2048 + vbase[p];
+    else return half * 2048 + (db >> 1) * 4096 + p * 1024 + vbase[p ^ (db & 1)];
+  };
+  // Copy instruction n = (wv*IPW + i) % NCP fills LDS bytes [1024 n, 1024 n + 1024)
+  // of a tile: lane takes the 16-byte piece whose slot is 64 n + lane.
+  int coff[IPW];
+  int crow[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int n = (wv * IPW + i) % NCP;
+    crow[i] = (64 / W) * (n % (W / 2)) + lane / W;
+    const int c = W * (n / (W / 2)) + ((lane % W) ^ lds_key<W>(crow[i]));
+    coff[i] = crow[i] * RB + c * 16;
+  }
+
+  // Current block: K/V bases (GL: rows below C from the first chunk, the rest
+  // from the second, whose base is already offset by -C rows).
+  const __bf16* Kbh = nullptr;
+  const __bf16* Vbh = nullptr;
+  const __bf16* Kbh_hi = nullptr;
+  const __bf16* Vbh_hi = nullptr;
+  auto tile_src = [&](const __bf16* lo, const __bf16* hi_, int j)
+                      __attribute__((always_inline)) -> const __bf16* {
+    const int u0 = j * 32;
+    return ((GL && u0 >= C) ? hi_ : lo) + (int64_t)u0 * D;
+  };
+  auto copy_full = [&](const __bf16* src, lds_char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      copy16_saddr((uint32_t)coff[i], src, lds_addr(dst + ((wv * IPW + i) % NCP) * 1024));
+  };
+  // Tile j that may run past the block end: rows past the end re-read the
+  // block's last row (masked later).
+  auto copy_any = [&](const __bf16* src, int j, lds_char* dst) __attribute__((always_inline)) {
+    const int last = Lk - 1 - j * 32;  // last valid tile row
+    if (last >= 31) {
+      copy_full(src, dst);
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int over = crow[i] - last;
+        copy16_saddr((uint32_t)(coff[i] - (over > 0 ? over : 0) * RB), src,
+                     lds_addr(dst + ((wv * IPW + i) % NCP) * 1024));
+      }
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  f32x16 s[2];            // scores of two tiles (S^T layout), by tile parity
+  bf16x8 pf[2][2];        // bf16 P of two tiles, by tile parity, key halves
+  float m2 = M_INIT;      // exponent reference (log2 units): an integer after the first tile
+  float L32 = 0.f;        // this lane's share of the fp32 row sum (gives lse)
+  // Row sums of the bf16 P (normalise O), accumulated on the matrix core as
+  // ones x P^T: every element of the 32x32 result holds the lane's query sum.
+  f32x16 lsum = {};
+  const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  float ts32;             // the lane's fp32 tile sum, added once the tile passed its check
+  const f32x16 zero16 = {};
+
+  // Weights of one tile at the current reference: P packed to bf16 for the
+  // PV product and the lane's fp32 sum.
+  auto softmax = [&](const f32x16& sj, bf16x8 (&pj)[2], float& t32)
+                     __attribute__((always_inline)) {
+    float a[4];
+    uint32_t pw[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sj[r], c_log2, -m2));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sj[r + 1], c_log2, -m2));
+      if (r < 4) {
+        a[r] = p0;
+        a[r + 1] = p1;
+      } else {
+        a[r & 3] += p0;
+        a[(r + 1) & 3] += p1;
+      }
+      pw[r >> 1] = cvt_pk_bf16(p0, p1);
+    }
+    t32 = (a[0] + a[1]) + (a[2] + a[3]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 q4 = {pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]};
+      pj[h] = __builtin_bit_cast(bf16x8, q4);
+    }
+  };
+  // The tile's exact row max raises the reference (to its ceiling) when it
+  // is above it; O and the running sums are rescaled by the power of two,
+  // then the tile's weights are recomputed.
+  auto reraise = [&](const f32x16& sj, bf16x8 (&pj)[2], float& t32)
+                     __attribute__((always_inline)) {
+    float mx = sj[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sj[r]);
+    mx = xhalf_max(mx) * c_log2;
+    const float m_new = mx > m2 ? ceilf(mx) : m2;
+    const int k = (int)fmaxf(m2 - m_new, -1000.f);
+    if (__ballot(k != 0)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_amdgcn_ldexpf(acc[db][r], k);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lsum[r] = __builtin_amdgcn_ldexpf(lsum[r], k);
+      L32 = __builtin_amdgcn_ldexpf(L32, k);
+    }
+    m2 = m_new;
+    softmax(sj, pj, t32);
+  };
+
+  auto qk_mfma = [&](const lds_char* Kt, f32x16& sj) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      sj = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+              Kt + (kk / KB) * BLK + kbase[kk % KB]),
+          qf[kk], kk == 0 ? zero16 : sj, 0, 0, 0);
+  };
+  auto pv_mfma = [&](const lds_char* Vt, const bf16x8 (&pj)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 0)));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 1)));
+        const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
+                                                          pj[half], acc[db], 0, 0, 0);
+      }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pj[half], lsum, 0, 0, 0);
+  };
+
+  for (int sb = 0; sb < nblk; ++sb) {
+    const int blk = (first + 1 + sb) % nblk;
+    if constexpr (GL) {
+      const int64_t lo_row = (int64_t)blk * C, hi_row = (int64_t)(2 * nblk - 1 - blk) * C - C;
+      Kbh = K + ((int64_t)bh * Lrow + lo_row) * D;
+      Vbh = V + ((int64_t)bh * Lrow + lo_row) * D;
+      Kbh_hi = K + ((int64_t)bh * Lrow + hi_row) * D;
+      Vbh_hi = V + ((int64_t)bh * Lrow + hi_row) * D;
+    } else {
+      Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
+      Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
+      Kbh_hi = Kbh;
+      Vbh_hi = Vbh;
+    }
+    // Tile counts.  n_main: tiles every row of the workgroup fully sees (the
+    // first row sees the fewest); n_tot: tiles with a key any of its rows
+    // sees.  The same per wave for the tail.
+    int n_main, n_tot, w_full, w_tot;
+    if (!causal) {
+      n_main = w_full = Lk / 32;
+      n_tot = w_tot = (Lk + 31) / 32;
+    } else {
+      int64_t c_g0, c_gl, c_w0, c_wl;
+      if constexpr (GL) {
+        c_g0 = zig_count_le(blk, nblk, C, pq_g0);
+        c_gl = zig_count_le(blk, nblk, C, pq_gl);
+        c_w0 = zig_count_le(blk, nblk, C, pq_w0);
+        c_wl = zig_count_le(blk, nblk, C, pq_wl);
+      } else {
+        const int64_t* kb_off = k_off + blk * koff_stride;
+        c_g0 = count_le(kb_off, Lk, pq_g0);
+        c_gl = count_le(kb_off, Lk, pq_gl);
+        c_w0 = count_le(kb_off, Lk, pq_w0);
+        c_wl = count_le(kb_off, Lk, pq_wl);
+      }
+      n_main = __builtin_amdgcn_readfirstlane((int)(c_g0 / 32));
+      n_tot = __builtin_amdgcn_readfirstlane((int)((c_gl + 31) / 32));
+      w_full = __builtin_amdgcn_readfirstlane((int)(c_w0 / 32));
+      w_tot = __builtin_amdgcn_readfirstlane((int)((c_wl + 31) / 32));
+    }
+    if (w0 >= Lq) w_full = w_tot = 0;  // a wave past the last row stores nothing
+    if (n_tot == 0) continue;          // no row of the workgroup sees this block
+
+    // ---- steady loop over tiles [0, n_main): every wave sees all of them ----
+    if (n_main > 0) {
+      const int last = n_main - 1;
+      auto kcopy = [&](int j, int buf) __attribute__((always_inline)) {
+        const int jj = j < last ? j : last;
+        copy_full(tile_src(Kbh, Kbh_hi, jj), Kl + buf * TB);
+      };
+      auto vcopy = [&](int j, int buf) __attribute__((always_inline)) {
+        const int jj = j < last ? j : last;
+        copy_full(tile_src(Vbh, Vbh_hi, jj), Vl + buf * TB);
+      };
+#pragma unroll
+      for (int j = 0; j < K_AHEAD; ++j) kcopy(j, j % NBUF);
+#pragma unroll
+      for (int j = 0; j < V_AHEAD; ++j) vcopy(j, j % NBUF);
+      // Iteration 0 runs the same body as the others: its PV(-1) multiplies
+      // zero weights into V(0), copied to the buffer tile -1 would use (so
+      // that no stale LDS value can turn 0 * x into NaN); the last
+      // iteration's QK^T of tile n_main reads a re-copied tile and is unused.
+      vcopy(0, NBUF - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[1][h][e] = (__bf16)0.0f;
+      wait_copies();
+      __syncthreads();
+      qk_mfma(Kl, s[0]);
+
+      // Iteration t: copies of K(t+3), V(t+2); PV(t-1) and QK^T(t+1) on the
+      // matrix cores next to the softmax of tile t; the overflow check.
+      auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
+        constexpr int P = decltype(P_)::value;
+        kcopy(t + K_AHEAD, (t + K_AHEAD) % NBUF);
+        vcopy(t + V_AHEAD, (t + V_AHEAD) % NBUF);
+        const lds_char* Vt = Vl + ((t + NBUF - 1) % NBUF) * TB;  // V(t-1)
+        const lds_char* Kt = Kl + ((t + 1) % NBUF) * TB;         // K(t+1)
+        constexpr int NPV = 2 * DB;   // PV(t-1) MFMAs
+        constexpr int NV = NPV + 2;   // ... and the row sums of P(t-1)
+        constexpr int NM = NV + KK;   // ... and QK^T(t+1)
+        auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+          if (i < NPV) {
+            const int half = i / DB, db = i % DB;
+            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 0)));
+            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 1)));
+            const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            return __builtin_bit_cast(bf16x8, v8);
+          }
+          if (i < NV) return ones8;
+          const int kk = i - NV;
+          return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+              Kt + (kk / KB) * BLK + kbase[kk % KB]);
+        };
+        // The iteration is emitted as NM chunks, each one MFMA (its operands
+        // read FWD_PF chunks ahead) and the softmax of some of the 16 score
+        // elements of tile t; scheduling barriers keep the chunks in order, so
+        // the exponentials and sums issue while the matrix core is busy.
+        float a4[4], pe[16];
+        uint32_t pw[8];  // P of tile t, bf16 pairs
+        auto element = [&](int r) __attribute__((always_inline)) {
+          pe[r] = __builtin_amdgcn_exp2f(fmaf(s[P][r], c_log2, -m2));
+          if (r < 4) a4[r] = pe[r];
+          else a4[r & 3] += pe[r];
+          if (r & 1) pw[r >> 1] = cvt_pk_bf16(pe[r - 1], pe[r]);
+        };
+        bf16x8 ob[FWD_PF];
+#pragma unroll
+        for (int i = 0; i < FWD_PF && i < NM; ++i) ob[i] = fetch(i);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          const bf16x8 cur = ob[i % FWD_PF];
+          if (i + FWD_PF < NM) ob[i % FWD_PF] = fetch(i + FWD_PF);
+          if (i < NPV) {
+            const int half = i / DB, db = i % DB;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][half], acc[db], 0, 0,
+                                                              0);
+          } else if (i < NV) {
+            lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][i - NPV], lsum, 0, 0, 0);
+          } else {
+            const int kk = i - NV;
+            s[P ^ 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[kk],
+                                                               kk == 0 ? zero16 : s[P ^ 1], 0, 0, 0);
+          }
+          // softmax elements of this chunk: [16 i / NM, 16 (i + 1) / NM)
+#pragma unroll
+          for (int r = (16 * i) / NM; r < (16 * (i + 1)) / NM; ++r) element(r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ts32 = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 q4 = {pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]};
+          pf[P][h] = __builtin_bit_cast(bf16x8, q4);
+        }
+        if (__ballot(ts32 > TILE_SUM_MAX)) reraise(s[P], pf[P], ts32);
+        L32 += ts32;
+        wait_copies_but<2 * IPW>();
+        __syncthreads();
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      int t = 0;
+      for (; t + 1 < n_main; t += 2) {
+        iter(t, I0{});
+        iter(t + 1, I1{});
+      }
+      // PV(last); its V tile landed two iterations ago.
+      if (t < n_main) {
+        iter(t, I0{});
+        pv_mfma(Vl + (last % NBUF) * TB, pf[0]);
+      } else {
+        pv_mfma(Vl + (last % NBUF) * TB, pf[1]);
+      }
+      wait_copies();  // redundant re-copies may still be in flight
+      __syncthreads();
+    }
+
+    // ---- tail: tiles [n_main, n_tot), per wave full, masked or skipped ----
+    if (n_tot > n_main) {
+      auto tcopy = [&](int j) __attribute__((always_inline)) {
+        const int buf = j % NBUF;
+        copy_any(tile_src(Kbh, Kbh_hi, j), j, Kl + buf * TB);
+        copy_any(tile_src(Vbh, Vbh_hi, j), j, Vl + buf * TB);
+      };
+      tcopy(n_main);
+      for (int t = n_main; t < n_tot; ++t) {
+        if (t + 1 < n_tot) {
+          tcopy(t + 1);
+          wait_copies_but<2 * IPW>();
+        } else {
+          wait_copies();
+        }
+        __syncthreads();
+        if (t < w_tot) {
+          const lds_char* Kt = Kl + (t % NBUF) * TB;
+          const lds_char* Vt = Vl + (t % NBUF) * TB;
+          qk_mfma(Kt, s[0]);
+          if (t >= w_full) {
+            const int u0 = t * 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int u = u0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+              bool vis = u < Lk;
+              if (causal && vis) {
+                int64_t kp;
+                if constexpr (GL) kp = zig(blk, u);
+                else kp = k_off[blk * koff_stride + u];
+                vis = kp <= my_qpos;
+              }
+              if (!vis) s[0][r] = -INFINITY;
+            }
+          }
+          reraise(s[0], pf[0], ts32);
+          L32 += ts32;
+          pv_mfma(Vt, pf[0]);
+        }
+      }
+      __syncthreads();  // the next block refills the buffers
+    }
+  }  // blocks
+
+  const float l16 = lsum[0];
+  const float l32 = xhalf_sum(L32);
+  if (qrow < Lq) {
+    const float inv = l16 > 0.f ? 1.f / l16 : 0.f;
+    const int64_t orow_i = GL ? zig(first, qrow) : qrow;
+    float* orow = Obh + orow_i * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 v = {acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv,
+                          acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
+        *reinterpret_cast<float4*>(orow + db * 32 + gq * 8 + hi * 4) = v;
+      }
+    if (hi == 0) lse_bh[orow_i] = l32 > 0.f ? (m2 + __log2f(l32)) * LN2 : -INFINITY;
+  }
+}
+
+template <bool GL, int W>
+hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int64_t* q_off,
+                         const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
+                         int64_t Lk, int64_t kv_stride, int64_t koff_stride, int nblk, int first,
+                         int D, bool causal, float scale, hipStream_t stream) {
+  const int n_qtiles = (int)((Lq + BM - 1) / BM);
+  const dim3 grid((unsigned)(n_qtiles * BH));
+  const float c_log2 = scale * LOG2E;
+  if (D == 128) {
+    hipLaunchKernelGGL((attn_fwd_kernel<128, GL, W>), grid, dim3(NTHREADS), 0, stream,
+                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
+                       BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0,
+                       c_log2, n_qtiles);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<64, GL, W>), grid, dim3(NTHREADS), 0, stream,
+                       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
+                       BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0,
+                       c_log2, n_qtiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V, const int64_t* q_off,
+                               const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
+                               int64_t Lk, int D, bool causal, float scale, hipStream_t stream) {
+  return launch_blocks<false, 4>(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, 0, 0, 1, 0, D, causal,
+                                 scale, stream);
+}
+
+hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_all,
+                            const int64_t* q_off, const int64_t* pos_all, float* O, float* lse,
+                            int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
+                            hipStream_t stream) {
+  return launch_blocks<false, 4>(Q_i, K_all, V_all, q_off, pos_all, O, lse, BH, Lr, Lr,
+                                 (int64_t)BH * Lr * D, Lr, N, i, D, causal, scale, stream);
+}
+
+hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, float* O, float* lse,
+                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
+                             hipStream_t stream) {
+  return launch_blocks<true, 8>(Q, K, V, nullptr, nullptr, O, lse, BH, Lr, Lr, 0, 0, N, i, D,
+                                causal, scale, stream);
+}
+
+}  // namespace cpa

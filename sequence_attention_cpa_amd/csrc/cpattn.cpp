@@ -352,7 +352,7 @@ cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, const 
     return fail(CPA_EINVAL, "lse must be 4-byte and pos_all 8-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
   for (int32_t r = rank_lo; r < rank_hi; ++r) {
-    const hipError_t e = cpa::launch_share_mfma(Q, K, V, pos_all, O, lse, B * H, Lr, N, r, D,
+    const hipError_t e = cpa::launch_share_mfma(Q, K, V, O, lse, B * H, Lr, N, r, D,
                                                 causal != 0, scale, (hipStream_t)stream);
     if (e != hipSuccess) return from_hip(e, "global-layout ring launch");
   }

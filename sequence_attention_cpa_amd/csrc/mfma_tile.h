@@ -16,6 +16,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int BN = 32;         // rows of one LDS tile (keys, or queries in the dK/dV pass)
@@ -64,6 +65,17 @@ __device__ inline int64_t count_le(const int64_t* __restrict__ off, int64_t n, i
   return lo + __popcll(__ballot(p));
 }
 
+// Two floats rounded to bf16 (nearest even) and packed, lo in bits 0-15, as
+// one v_cvt_pk_bf16_f32.  The empty asm makes the packed word opaque: without
+// it the compiler rewrites later shifts and masks of the word into separate
+// single-element conversions.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2 pr = {(__bf16)lo, (__bf16)hi};
+  uint32_t w = __builtin_bit_cast(uint32_t, pr);
+  asm("" : "+v"(w));
+  return w;
+}
+
 __device__ __forceinline__ float xhalf_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -94,6 +106,12 @@ __device__ __forceinline__ void copy16_vaddr(const void* gptr, uint32_t lds) {
                : "memory");
 }
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order, so every older copy has landed).
+template <int N>
+__device__ __forceinline__ void wait_copies_but() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
