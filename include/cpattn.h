@@ -133,6 +133,25 @@ cpa_status cpa_rank_forward(int32_t i, int32_t N, const void *Q_i, const void *K
                             size_t ws_bytes, void *stream);
 
 /*
+ * cpa_rank_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partial of each ring step goes to a
+ * 16 MiB scratch array inside the library, one per GPU, held until the
+ * process ends; the rank's rows are worked in slices that fit it (whole heads
+ * when a head's partial fits, else row ranges of one head), so no size is
+ * refused for its sake.  The call itself allocates nothing.  Arguments,
+ * results and errors as for cpa_rank_forward; N == 1 uses no scratch.  Every
+ * call on one GPU shares that GPU's scratch: calls that can overlap on one
+ * GPU (different streams without ordering) race and must be serialised by
+ * the caller.  The scratch is written before it is read in every call, so
+ * nothing carries over from one call to the next.
+ */
+cpa_status cpa_rank_forward_noalloc(int32_t i, int32_t N, const void *Q_i, const void *K_all,
+                                    const void *V_all, const int64_t *pos_all, cpa_dtype dt,
+                                    int32_t B, int32_t H, int64_t L, int32_t D, int32_t causal,
+                                    float scale, float *O_i, float *lse_i, void *stream);
+
+/*
  * Rank i's whole ring in ONE launch: the same result as cpa_rank_forward (up
  * to rounding order), but the kernel walks the N K/V blocks itself and keeps
  * the online-softmax state (O, running max, sums) in registers from one block

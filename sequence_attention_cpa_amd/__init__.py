@@ -14,7 +14,7 @@ from ._lib import (CPA_BF16, CPA_EDTYPE, CPA_EINVAL, CPA_ESHAPE, CPA_F32,  # noq
                    version)
 
 __all__ = ["zigzag_layout", "partial", "merge", "rank_forward_workspace", "rank_forward",
-           "rank_forward_fused", "share_forward", "share_backward", "zigzag_permute", "rope",
+           "rank_forward_noalloc", "rank_forward_fused", "share_forward", "share_backward", "zigzag_permute", "rope",
            "zigzag_permute_rope", "backward_delta", "partial_backward", "rank_backward",
            "check_offsets", "debug_offsets", "last_error", "version", "CpaError", "CPA_ROPE_INTERLEAVED", "CPA_ROPE_HALF"]
 
@@ -197,6 +197,27 @@ def rank_forward(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool, scale
                                   _dtype_code(Q_i), B, H, L, D, int(bool(causal)), float(scale),
                                   _ptr(out), _ptr(lse), _ptr(workspace),
                                   0 if workspace is None else workspace.numel(), _stream(Q_i)))
+    return out, lse
+
+
+def rank_forward_noalloc(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
+                         scale: float = 0.0, out=None, lse=None):
+    """rank_forward with the partial kept in the library's per-GPU scratch
+    instead of a workspace (the C call allocates nothing; out/lse are made
+    here only when not given)."""
+    torch = _torch()
+    B, H, Lr, D = Q_i.shape
+    if out is None:
+        out = torch.empty((B, H, Lr, D), dtype=torch.float32, device=Q_i.device)
+    if lse is None:
+        lse = torch.empty((B, H, Lr), dtype=torch.float32, device=Q_i.device)
+    _check_rank_major(Q_i, K_all, V_all, pos_all, N, out, lse)
+    _need_gpu(Q_i, K_all, V_all, pos_all, out, lse)
+    _debug_check(causal, pos_all=pos_all)
+    check(load().cpa_rank_forward_noalloc(i, N, _ptr(Q_i), _ptr(K_all), _ptr(V_all),
+                                          _ptr(pos_all), _dtype_code(Q_i), B, H, Lr * N, D,
+                                          int(bool(causal)), float(scale), _ptr(out), _ptr(lse),
+                                          _stream(Q_i)))
     return out, lse
 
 

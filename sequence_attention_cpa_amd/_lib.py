@@ -31,6 +31,9 @@ SIGNATURES = {
     "cpa_rank_forward_workspace": (_sz, [_i32, _i32, _i64, _i32, _i32]),
     "cpa_rank_forward": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32,
                                         _i64, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "cpa_rank_forward_noalloc": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_int,
+                                                _i32, _i32, _i64, _i32, _i32, _f32, _vp, _vp,
+                                                _vp]),
     "cpa_rank_forward_fused": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
                                               _i32, _i64, _i32, _i32, _f32, _vp, _vp, _vp]),
     "cpa_share_forward": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32,

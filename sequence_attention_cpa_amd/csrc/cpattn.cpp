@@ -8,7 +8,16 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+
+// Device scratch of cpa_rank_forward_noalloc: the partial (O, lse) of one
+// slice of a rank's rows.  Every GPU the library runs on holds its own copy
+// for the life of the process; host code reaches it only through the address
+// hipGetSymbolAddress returns for that device (the name is a host-side
+// stand-in, not a device address).
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -131,6 +140,33 @@ cpa_status check_rope(cpa_dtype dt, int32_t B, int32_t H, int32_t D, double base
   return CPA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Address of `scratch` on the device that runs `stream` (the current device
+// for the null stream), looked up once per device with that device current.
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int prev = -1;
+    hipError_t r = hipGetDevice(&prev);
+    if (r == hipSuccess && prev != dev) r = hipSetDevice(dev);
+    if (r == hipSuccess) r = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    if (prev >= 0 && prev != dev) {
+      const hipError_t r2 = hipSetDevice(prev);
+      if (r == hipSuccess) r = r2;
+    }
+    g_scratch_err[dev] = r;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +267,65 @@ cpa_status cpa_rank_forward(int32_t i, int32_t N, const void* Q_i, const void* K
       if (st != CPA_OK) return st;
       st = from_hip(cpa::launch_merge(O_i, lse_i, tO, tl, (int64_t)rows, D, hs), "merge launch");
       if (st != CPA_OK) return st;
+    }
+  }
+  return ok();
+}
+
+cpa_status cpa_rank_forward_noalloc(int32_t i, int32_t N, const void* Q_i, const void* K_all,
+                                    const void* V_all, const int64_t* pos_all, cpa_dtype dt,
+                                    int32_t B, int32_t H, int64_t L, int32_t D, int32_t causal,
+                                    float scale, float* O_i, float* lse_i, void* stream) {
+  cpa_status st = check_rank_shape(N, L, B, H, D);
+  if (st != CPA_OK) return st;
+  if (i < 0 || i >= N) return fail(CPA_EINVAL, "rank index %d outside [0, %d)", i, N);
+  if (!pos_all) return fail(CPA_EINVAL, "null pos_all");
+  const int64_t Lr = L / N;
+  st = check_partial(Q_i, K_all, V_all, dt, B, H, Lr, Lr, D, pos_all, pos_all, causal, O_i, lse_i);
+  if (st != CPA_OK) return st;
+  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, 0);
+  if (st != CPA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = nullptr;
+  if (N > 1) {
+    void* p = nullptr;
+    const hipError_t e = noalloc_scratch(hs, &p);
+    if (e != hipSuccess) return from_hip(e, "device scratch lookup");
+    ws = (char*)p;
+  }
+  // The partial of a slice fits the scratch: whole heads at a time when a
+  // head does (O at the start, lse 256-byte aligned after it), else row
+  // ranges of one head.
+  const int64_t cap = (int64_t)((kNoallocScratchBytes - 512) / ((size_t)(D + 1) * 4));
+  const int64_t BH = (int64_t)B * H;
+  const int64_t heads_per = Lr <= cap ? (BH < cap / Lr ? BH : cap / Lr) : 1;
+  const int64_t rows_per = Lr <= cap ? Lr : cap;
+  const size_t esz = dt == CPA_BF16 ? 2 : 4;
+  for (int64_t h0 = 0; h0 < BH; h0 += heads_per) {
+    const int64_t nh = BH - h0 < heads_per ? BH - h0 : heads_per;
+    for (int64_t r0 = 0; r0 < Lr; r0 += rows_per) {
+      const int64_t nr = Lr - r0 < rows_per ? Lr - r0 : rows_per;
+      const int64_t row0 = h0 * Lr + r0;  // first O row of the slice
+      const char* Qs = (const char*)Q_i + (size_t)row0 * D * esz;
+      float* Os = O_i + row0 * D;
+      float* ls = lse_i + row0;
+      const int64_t* q_off = pos_all + (int64_t)i * Lr + r0;
+      float* tO = (float*)ws;
+      float* tl = (float*)(ws + ((size_t)(nh * nr) * D * 4 + 255) / 256 * 256);
+      for (int32_t s = 0; s < N; ++s) {
+        const int32_t j = (i + s) % N;  // ring order: own block first, then i+1, i+2, ...
+        const size_t blk = ((size_t)j * BH + h0) * Lr * D * esz;
+        const char* Kj = (const char*)K_all + blk;
+        const char* Vj = (const char*)V_all + blk;
+        const int64_t* k_off = pos_all + (int64_t)j * Lr;
+        st = enqueue_partial(Qs, Kj, Vj, dt, 1, (int32_t)nh, nr, Lr, D, q_off, k_off, causal,
+                             scale, s == 0 ? Os : tO, s == 0 ? ls : tl, hs);
+        if (st != CPA_OK) return st;
+        if (s > 0) {
+          st = from_hip(cpa::launch_merge(Os, ls, tO, tl, nh * nr, D, hs), "merge launch");
+          if (st != CPA_OK) return st;
+        }
+      }
     }
   }
   return ok();

@@ -168,6 +168,33 @@ def test_rank_forward_rejects(lib, kw, status):
     assert cpa.last_error() != ""
 
 
+def _noalloc(lib, **kw):
+    a = dict(i=0, N=4, Q=P, K=P, V=P, pos=P, dt=_lib.CPA_BF16, B=1, H=2, L=256, D=128, causal=1,
+             scale=0.0, O=P, lse=P, stream=None)
+    a.update(kw)
+    return lib.cpa_rank_forward_noalloc(a["i"], a["N"], a["Q"], a["K"], a["V"], a["pos"], a["dt"],
+                                        a["B"], a["H"], a["L"], a["D"], a["causal"], a["scale"],
+                                        a["O"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(i=4), _lib.CPA_EINVAL),
+    (dict(i=-1), _lib.CPA_EINVAL),
+    (dict(N=0), _lib.CPA_EINVAL),
+    (dict(L=260), _lib.CPA_ESHAPE),
+    (dict(D=48), _lib.CPA_EUNSUPPORTED),
+    (dict(dt=2), _lib.CPA_EDTYPE),
+    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(Q=P + 2), _lib.CPA_EINVAL),
+    (dict(O=None), _lib.CPA_EINVAL),
+])
+def test_rank_forward_noalloc_rejects(lib, kw, status):
+    """Host-side checks of the no-allocation ring run before the device scratch
+    is looked up, so they need no GPU."""
+    assert _noalloc(lib, **kw) == status
+    assert cpa.last_error() != ""
+
+
 def _fused(lib, **kw):
     a = dict(i=0, N=4, Q=P, K=P, V=P, pos=P, dt=_lib.CPA_BF16, B=1, H=2, L=256, D=128, causal=1,
              scale=0.0, O=P, lse=P, stream=None)
