@@ -219,7 +219,7 @@ def main():
 
     share_evs = []
     if global_ok:
-        share_evs = timed(lambda: cpa.share_forward(Q, K, V, pos_d, w.N, w.causal,
+        share_evs = timed(lambda: cpa.share_forward(Q, K, V, w.N, w.causal,
                                                     rank_lo=rank, rank_hi=rank + 1, out=pipe.O,
                                                     lse=pipe.lse), reps)
     fused_evs, last_evs = [], []
@@ -268,7 +268,7 @@ def main():
         pipe.backward(dO)
         if pipe.global_layout:
             gbwd_evs = timed(lambda: cpa.share_backward(
-                Q, K, V, pos_d, pipe.O, dO, pipe.lse, w.N, w.causal, pipe.dK, pipe.dV,
+                Q, K, V, pipe.O, dO, pipe.lse, w.N, w.causal, pipe.dK, pipe.dV,
                 pipe.scale, rank, rank + 1, dQ=pipe.dQ, delta=pipe.delta), reps)
         zigzag(pipe.O, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=rk.Or)
         zigzag(pipe.lse, pos_d, w.N, rank_lo=rank, rank_hi=rank + 1, out=rk.lser)

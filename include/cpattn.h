@@ -176,19 +176,20 @@ cpa_status cpa_rank_forward_fused(int32_t i, int32_t N, const void *Q_i, const v
  * for u < C, chunk 2N-1-r after, C = L/(2N)), so Q, K, V are read and O, lse
  * written in global token order without separate permute passes ("序列与上下文
  * 并行", 上下文并行 and 工程实践: the Z-shaped assignment, global positions).
+ * A token's position is its global index, so the causal bounds are the
+ * zigzag closed form; no position table is taken, and no table can disagree
+ * with the addressing.
  *   Q, K, V    device [B, H, L, D] bf16, global order
- *   pos_all    device int64 [N, L/N]: cpa_zigzag_layout(L, N)'s table
- *              (precondition; it supplies the causal bounds)
  *   O, lse     device float32 [B, H, L, D] / [B, H, L]: the selected ranks'
  *              rows are written, the others are left untouched
  *   causal, scale   as for cpa_partial
  * bf16 with D = 64 or 128 and C a multiple of 32 (CPA_EUNSUPPORTED otherwise;
  * use the permute + cpa_rank_forward_fused path).  One launch per rank.
  */
-cpa_status cpa_share_forward(const void *Q, const void *K, const void *V, const int64_t *pos_all,
-                             cpa_dtype dt, int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
-                             int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
-                             float *O, float *lse, void *stream);
+cpa_status cpa_share_forward(const void *Q, const void *K, const void *V, cpa_dtype dt, int32_t B,
+                             int32_t H, int64_t L, int32_t D, int32_t N, int32_t rank_lo,
+                             int32_t rank_hi, int32_t causal, float scale, float *O, float *lse,
+                             void *stream);
 
 /*
  * Permutation between global order and rank-major zigzag order, for ranks
@@ -275,11 +276,11 @@ cpa_status cpa_rank_backward(int32_t i, int32_t N, const void *Q_i, const void *
  * The ranks' ring backward directly on global-order data: cpa_rank_backward
  * for each rank r in [rank_lo, rank_hi), with the zigzag permute folded into
  * the kernels' addressing as in cpa_share_forward (rank r's local row u is
- * global row zig(r, u)), so no tensor is permuted before or after.
+ * global row zig(r, u), and a token's position is its global index), so no
+ * tensor is permuted before or after and no position table is taken.
  *   Q, K, V, dO   device [B, H, L, D] bf16, global order
  *   O, lse        device float32 [B, H, L, D] / [B, H, L]: the forward's
  *                 output in global order (cpa_share_forward)
- *   pos_all       device int64 [N, L/N]: cpa_zigzag_layout(L, N)'s table
  *   dQ            device float32 [B, H, L, D]: the selected ranks' rows are
  *                 WRITTEN, the others are left untouched
  *   dK, dV        device float32 [B, H, L, D]: the selected ranks'
@@ -292,11 +293,11 @@ cpa_status cpa_rank_backward(int32_t i, int32_t N, const void *Q_i, const void *
  * otherwise; use the permute + cpa_rank_backward path).  Three launches per
  * rank: delta, the dQ pass and the dK/dV pass.
  */
-cpa_status cpa_share_backward(const void *Q, const void *K, const void *V, const int64_t *pos_all,
-                              const float *O, const void *dO, const float *lse, cpa_dtype dt,
-                              int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
-                              int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
-                              float *dQ, float *dK, float *dV, float *delta, void *stream);
+cpa_status cpa_share_backward(const void *Q, const void *K, const void *V, const float *O,
+                              const void *dO, const float *lse, cpa_dtype dt, int32_t B,
+                              int32_t H, int64_t L, int32_t D, int32_t N, int32_t rank_lo,
+                              int32_t rank_hi, int32_t causal, float scale, float *dQ, float *dK,
+                              float *dV, float *delta, void *stream);
 
 /* Pairing of the elements a rotary embedding rotates together. */
 typedef enum {

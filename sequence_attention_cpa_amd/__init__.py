@@ -109,6 +109,16 @@ def _debug_check(causal, **tables):
                                        f"{i % n} does not exceed the entry before it")
 
 
+def _debug_range(pos_all, L):
+    """Debug mode only: the permutes index rows by position, so every entry of
+    the table must lie in [0, L) (reads the answer back: synchronises)."""
+    if not _debug_offsets or pos_all.numel() == 0:
+        return
+    lo, hi = int(pos_all.min().item()), int(pos_all.max().item())
+    if lo < 0 or hi >= L:
+        raise CpaError(CPA_EINVAL, f"pos_all has entries outside [0, {L}): min {lo}, max {hi}")
+
+
 def zigzag_layout(L: int, N: int):
     """int64 CPU tensor [N, L/N] of global token positions per rank (host call)."""
     torch = _torch()
@@ -239,11 +249,12 @@ def rank_forward_fused(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
     return out, lse
 
 
-def share_forward(Q, K, V, pos_all, N: int, causal: bool, scale: float = 0.0, rank_lo: int = 0,
+def share_forward(Q, K, V, N: int, causal: bool, scale: float = 0.0, rank_lo: int = 0,
                   rank_hi: int | None = None, out=None, lse=None):
     """Rings of ranks [rank_lo, rank_hi) on global-order Q/K/V [B,H,L,D] (bf16):
     O [B,H,L,D] and lse [B,H,L] float32 in global order, the selected ranks'
-    rows written (the zigzag permute folded into the kernel's addressing)."""
+    rows written (the zigzag permute folded into the kernel's addressing, a
+    token's position its global index: no position table)."""
     torch = _torch()
     rank_hi = N if rank_hi is None else rank_hi
     B, H, L, D = Q.shape
@@ -254,18 +265,16 @@ def share_forward(Q, K, V, pos_all, N: int, causal: bool, scale: float = 0.0, ra
     dt, f32 = (Q.dtype,), (torch.float32,)
     _expect(K, (B, H, L, D), dt, "K")
     _expect(V, (B, H, L, D), dt, "V")
-    _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _expect(out, (B, H, L, D), f32, "out")
     _expect(lse, (B, H, L), f32, "lse")
-    _need_gpu(Q, K, V, pos_all, out, lse)
-    _debug_check(causal, pos_all=pos_all)
-    check(load().cpa_share_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _dtype_code(Q), B, H,
-                                   L, D, N, rank_lo, rank_hi, int(bool(causal)), float(scale),
-                                   _ptr(out), _ptr(lse), _stream(Q)))
+    _need_gpu(Q, K, V, out, lse)
+    check(load().cpa_share_forward(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, L, D, N,
+                                   rank_lo, rank_hi, int(bool(causal)), float(scale), _ptr(out),
+                                   _ptr(lse), _stream(Q)))
     return out, lse
 
 
-def share_backward(Q, K, V, pos_all, O, dO, lse, N: int, causal: bool, dK, dV,
+def share_backward(Q, K, V, O, dO, lse, N: int, causal: bool, dK, dV,
                    scale: float = 0.0, rank_lo: int = 0, rank_hi: int | None = None, dQ=None,
                    delta=None):
     """Ring backward of ranks [rank_lo, rank_hi) on global-order bf16 Q/K/V/dO
@@ -286,10 +295,8 @@ def share_backward(Q, K, V, pos_all, O, dO, lse, N: int, causal: bool, dK, dV,
         _expect(t, (B, H, L, D), f32, n)
     _expect(lse, (B, H, L), f32, "lse")
     _expect(delta, (B, H, L), f32, "delta")
-    _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
-    _need_gpu(Q, K, V, pos_all, O, dO, lse, dK, dV, dQ, delta)
-    _debug_check(causal, pos_all=pos_all)
-    check(load().cpa_share_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(pos_all), _ptr(O), _ptr(dO),
+    _need_gpu(Q, K, V, O, dO, lse, dK, dV, dQ, delta)
+    check(load().cpa_share_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
                                     _ptr(lse), _dtype_code(Q), B, H, L, D, N, rank_lo, rank_hi,
                                     int(bool(causal)), float(scale), _ptr(dQ), _ptr(dK), _ptr(dV),
                                     _ptr(delta), _stream(Q)))
@@ -319,11 +326,14 @@ def zigzag_permute(src, pos_all, N: int, inverse: bool = False, rank_lo: int = 0
             shape = (nr, B, H, Lr) if squeeze else (nr, B, H, Lr, D)
             out = torch.empty(shape, dtype=src.dtype, device=src.device)
     if inverse:
+        # the source must hold exactly the selected ranks: the library reads nr of them
+        _expect(src, (nr, B, H, Lr) if squeeze else (nr, B, H, Lr, D), (src.dtype,), "src")
         _expect(out, (B, H, L) if squeeze else (B, H, L, D), (src.dtype,), "out")
     else:
         _expect(out, (nr, B, H, Lr) if squeeze else (nr, B, H, Lr, D), (src.dtype,), "out")
     _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _need_gpu(src, pos_all, out)
+    _debug_range(pos_all, L)
     check(load().cpa_zigzag_permute(_ptr(src), _ptr(out), src.element_size(), B, H, L, D,
                                     _ptr(pos_all), N, rank_lo, rank_hi, int(bool(inverse)),
                                     _stream(src)))
@@ -358,6 +368,7 @@ def zigzag_permute_rope(src, pos_all, N: int, base: float = 10000.0,
     _expect(out, (rank_hi - rank_lo, B, H, L // max(N, 1), D), (src.dtype,), "out")
     _expect(pos_all, (N, L // max(N, 1)), (torch.int64,), "pos_all")
     _need_gpu(src, pos_all, out)
+    _debug_range(pos_all, L)
     check(load().cpa_zigzag_permute_rope(_ptr(src), _ptr(out), _dtype_code(src), B, H, L, D,
                                          _ptr(pos_all), N, rank_lo, rank_hi, float(base),
                                          int(pairing), _stream(src)))

@@ -36,7 +36,7 @@ SIGNATURES = {
                                                 _vp]),
     "cpa_rank_forward_fused": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
                                               _i32, _i64, _i32, _i32, _f32, _vp, _vp, _vp]),
-    "cpa_share_forward": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32,
+    "cpa_share_forward": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32,
                                          _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "cpa_zigzag_permute": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _i32,
                                           _i32, _i32, _i32, _vp]),
@@ -47,7 +47,7 @@ SIGNATURES = {
     "cpa_rank_backward": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          ctypes.c_int, _i32, _i32, _i64, _i32, _i32, _f32, _vp, _vp,
                                          _vp, _vp, _vp]),
-    "cpa_share_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+    "cpa_share_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
                                           _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                           _vp, _vp, _vp, _vp]),
     "cpa_rope": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _i32, _i64, _i32, _vp, _f64, _i32,

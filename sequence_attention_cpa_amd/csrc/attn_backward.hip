@@ -205,13 +205,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   const int64_t qrow_c = qrow < Lq ? qrow : Lq - 1;
   const float c_log2 = scale * LOG2E;
 
-  const int64_t q_first = causal ? q_off[q_base] : 0;
-  const int64_t q_last = causal ? q_off[last_row] : 0;
-  const int64_t my_qpos = causal ? q_off[qrow_c] : 0;
   const int64_t Lrow = GL ? Lq * nblk : Lq;  // rows per head of Q, dO, lse, delta, dQ
   auto qmap = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
     return GL ? zig_row(first, u, Lq, nblk) : u;
   };
+  // Query positions: GL rows are their own positions (the zigzag closed form).
+  auto qpos = [&](int64_t u) __attribute__((always_inline)) -> int64_t {
+    return GL ? qmap(u) : q_off[u];
+  };
+  const int64_t q_first = causal ? qpos(q_base) : 0;
+  const int64_t q_last = causal ? qpos(last_row) : 0;
+  const int64_t my_qpos = causal ? qpos(qrow_c) : 0;
   const int64_t qg = (int64_t)bh * Lrow + qmap(qrow_c);
   const float l2 = lse_ref(lse[qg]);
   const float dl = delta[qg];
@@ -316,15 +320,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
       Vbh_hi = Vbh;
     }
     if (causal) {
-      const int64_t* kb_off = k_off + blk * koff_stride;
-      n_lo = count_le(kb_off, Lk, q_first);
-      n_hi = count_le(kb_off, Lk, q_last);
-      int64_t lo = n_lo, hb = n_hi;
-      while (lo < hb) {
-        const int64_t mid = (lo + hb) >> 1;
-        if (kb_off[mid] <= my_qpos) lo = mid + 1; else hb = mid;
+      if constexpr (GL) {
+        const int64_t C = Lk / 2;
+        n_lo = zig_count_le(blk, nblk, C, q_first);
+        n_hi = zig_count_le(blk, nblk, C, q_last);
+        my_n = zig_count_le(blk, nblk, C, my_qpos);
+      } else {
+        const int64_t* kb_off = k_off + blk * koff_stride;
+        n_lo = count_le(kb_off, Lk, q_first);
+        n_hi = count_le(kb_off, Lk, q_last);
+        int64_t lo = n_lo, hb = n_hi;
+        while (lo < hb) {
+          const int64_t mid = (lo + hb) >> 1;
+          if (kb_off[mid] <= my_qpos) lo = mid + 1; else hb = mid;
+        }
+        my_n = lo;
       }
-      my_n = lo;
     }
     if (n_hi == 0) continue;
     T = (int)((n_hi + BN - 1) / BN);
@@ -431,16 +442,22 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   // this lane's key's.
   int64_t m_lo = 0, m_hi = 0, my_first = 0;
   if (causal) {
-    const int64_t* kb_off = k_off + blk * koff_stride;
-    m_lo = count_le(q_off, Lq, kb_off[k_base] - 1);
-    m_hi = count_le(q_off, Lq, kb_off[last_key] - 1);
-    const int64_t kp = kb_off[krow_c];
-    int64_t lo = m_lo, hb = m_hi;  // first t in [m_lo, m_hi] with position >= kp
-    while (lo < hb) {
-      const int64_t mid = (lo + hb) >> 1;
-      if (q_off[mid] < kp) lo = mid + 1; else hb = mid;
+    if constexpr (GL) {  // positions are the zigzag closed form
+      m_lo = zig_count_le(qrank, nblk, Cq, kmap(k_base) - 1);
+      m_hi = zig_count_le(qrank, nblk, Cq, kmap(last_key) - 1);
+      my_first = zig_count_le(qrank, nblk, Cq, kmap(krow_c) - 1);
+    } else {
+      const int64_t* kb_off = k_off + blk * koff_stride;
+      m_lo = count_le(q_off, Lq, kb_off[k_base] - 1);
+      m_hi = count_le(q_off, Lq, kb_off[last_key] - 1);
+      const int64_t kp = kb_off[krow_c];
+      int64_t lo = m_lo, hb = m_hi;  // first t in [m_lo, m_hi] with position >= kp
+      while (lo < hb) {
+        const int64_t mid = (lo + hb) >> 1;
+        if (q_off[mid] < kp) lo = mid + 1; else hb = mid;
+      }
+      my_first = lo;
     }
-    my_first = lo;
   }
   if (m_lo >= Lq) return;  // no query sees any key of this workgroup: nothing to add
   const int t0 = (int)(m_lo / BN);
@@ -857,14 +874,14 @@ hipError_t launch_bwd_mfma(const void* Q, const void* K, const void* V, const vo
 }
 
 hipError_t launch_bwd_share_mfma(const void* Q, const void* K, const void* V, const void* dO,
-                                 const float* lse, const float* delta, const int64_t* pos_all,
-                                 float* dQ, float* dK, float* dV, int BH, int64_t Lr, int N, int i,
-                                 int D, bool causal, float scale, hipStream_t stream) {
+                                 const float* lse, const float* delta, float* dQ, float* dK,
+                                 float* dV, int BH, int64_t Lr, int N, int i, int D, bool causal,
+                                 float scale, hipStream_t stream) {
   if (D == 128)
-    return mfma_bwd<128, true>(Q, K, V, dO, lse, delta, pos_all + (int64_t)i * Lr, pos_all, dQ,
-                               dK, dV, BH, Lr, Lr, 0, Lr, N, i, causal, scale, false, stream);
-  return mfma_bwd<64, true>(Q, K, V, dO, lse, delta, pos_all + (int64_t)i * Lr, pos_all, dQ, dK,
-                            dV, BH, Lr, Lr, 0, Lr, N, i, causal, scale, false, stream);
+    return mfma_bwd<128, true>(Q, K, V, dO, lse, delta, nullptr, nullptr, dQ, dK, dV, BH, Lr, Lr,
+                               0, 0, N, i, causal, scale, false, stream);
+  return mfma_bwd<64, true>(Q, K, V, dO, lse, delta, nullptr, nullptr, dQ, dK, dV, BH, Lr, Lr, 0,
+                            0, N, i, causal, scale, false, stream);
 }
 
 hipError_t launch_bwd_rowwise(const void* Q, const void* K, const void* V, const void* dO,

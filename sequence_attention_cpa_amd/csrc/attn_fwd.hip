@@ -107,14 +107,6 @@ __device__ __forceinline__ int lds_slot(int r, int c) {
   return 32 * W * (c / W) + W * r + ((c % W) ^ lds_key<W>(r));
 }
 
-// Number of keys of a zigzag block (rank b's rows: chunk b, then chunk
-// 2N-1-b, C rows each) at positions <= x.
-__device__ __forceinline__ int64_t zig_count_le(int b, int nblk, int64_t C, int64_t x) {
-  const int64_t lo = x - (int64_t)b * C + 1;
-  const int64_t hi = x - (int64_t)(2 * nblk - 1 - b) * C + 1;
-  return (lo < 0 ? 0 : (lo > C ? C : lo)) + (hi < 0 ? 0 : (hi > C ? C : hi));
-}
-
 // Blocks: the queries meet nblk K/V blocks of Lk rows each, block b at
 // K + b * kv_stride (V likewise) with positions k_off + b * koff_stride, in
 // the order b = first + 1, first + 2, ..., first (mod nblk).  One block is one

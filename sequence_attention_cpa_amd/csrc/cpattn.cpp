@@ -420,8 +420,8 @@ cpa_status cpa_zigzag_permute_rope(const void* src, void* dst, cpa_dtype dt, int
                   "permute+rope launch");
 }
 
-cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, const int64_t* pos_all,
-                             cpa_dtype dt, int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
+                             int32_t H, int64_t L, int32_t D, int32_t N,
                              int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
                              float* O, float* lse, void* stream) {
   if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
@@ -440,11 +440,10 @@ cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, const 
   if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
   st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, 0);
   if (st != CPA_OK) return st;
-  if (!Q || !K || !V || !pos_all || !O || !lse) return fail(CPA_EINVAL, "null pointer");
+  if (!Q || !K || !V || !O || !lse) return fail(CPA_EINVAL, "null pointer");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
     return fail(CPA_EINVAL, "Q, K, V and O must be 16-byte aligned");
-  if (!aligned(lse, 4) || !aligned(pos_all, 8))
-    return fail(CPA_EINVAL, "lse must be 4-byte and pos_all 8-byte aligned");
+  if (!aligned(lse, 4)) return fail(CPA_EINVAL, "lse must be 4-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
   for (int32_t r = rank_lo; r < rank_hi; ++r) {
     const hipError_t e = cpa::launch_share_mfma(Q, K, V, O, lse, B * H, Lr, N, r, D,
@@ -541,8 +540,8 @@ cpa_status cpa_rank_backward(int32_t i, int32_t N, const void* Q_i, const void* 
   return ok();
 }
 
-cpa_status cpa_share_backward(const void* Q, const void* K, const void* V, const int64_t* pos_all,
-                              const float* O, const void* dO, const float* lse, cpa_dtype dt,
+cpa_status cpa_share_backward(const void* Q, const void* K, const void* V, const float* O,
+                              const void* dO, const float* lse, cpa_dtype dt,
                               int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
                               int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
                               float* dQ, float* dK, float* dV, float* delta, void* stream) {
@@ -562,20 +561,20 @@ cpa_status cpa_share_backward(const void* Q, const void* K, const void* V, const
   if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
   st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, N);
   if (st != CPA_OK) return st;
-  if (!Q || !K || !V || !pos_all || !O || !dO || !lse || !dQ || !dK || !dV || !delta)
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !delta)
     return fail(CPA_EINVAL, "null pointer");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
       !aligned(dO, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16))
     return fail(CPA_EINVAL, "Q, K, V, O, dO, dQ, dK and dV must be 16-byte aligned");
-  if (!aligned(lse, 4) || !aligned(delta, 4) || !aligned(pos_all, 8))
-    return fail(CPA_EINVAL, "lse and delta must be 4-byte and pos_all 8-byte aligned");
+  if (!aligned(lse, 4) || !aligned(delta, 4))
+    return fail(CPA_EINVAL, "lse and delta must be 4-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
   const int BH = B * H;
   hipStream_t s = (hipStream_t)stream;
   for (int32_t r = rank_lo; r < rank_hi; ++r) {
     hipError_t e = cpa::launch_bwd_delta_share(O, dO, BH, Lr, N, r, D, delta, s);
     if (e != hipSuccess) return from_hip(e, "backward delta launch");
-    e = cpa::launch_bwd_share_mfma(Q, K, V, dO, lse, delta, pos_all, dQ, dK, dV, BH, Lr, N, r, D,
+    e = cpa::launch_bwd_share_mfma(Q, K, V, dO, lse, delta, dQ, dK, dV, BH, Lr, N, r, D,
                                    causal != 0, scale, s);
     if (e != hipSuccess) return from_hip(e, "global-layout ring backward launch");
   }

@@ -44,6 +44,18 @@ __device__ __forceinline__ int swz(int r, int c) {
   }
 }
 
+// Zigzag layout, closed form: rank r of nblk holds chunk r, then chunk
+// 2nblk-1-r, C rows each.  Its local row u is global row (and position)
+// zig_pos(r, u); zig_count_le counts its rows at positions <= x.
+__device__ __forceinline__ int64_t zig_pos(int r, int64_t u, int64_t C, int nblk) {
+  return u < C ? (int64_t)r * C + u : (int64_t)(2 * nblk - 1 - r) * C + (u - C);
+}
+__device__ __forceinline__ int64_t zig_count_le(int r, int nblk, int64_t C, int64_t x) {
+  const int64_t lo = x - (int64_t)r * C + 1;
+  const int64_t hi = x - (int64_t)(2 * nblk - 1 - r) * C + 1;
+  return (lo < 0 ? 0 : (lo > C ? C : lo)) + (hi < 0 ? 0 : (hi > C ? C : hi));
+}
+
 // Number of entries <= x in the increasing array off[0, n); wave-cooperative
 // 64-way search (every lane returns the same value).
 __device__ inline int64_t count_le(const int64_t* __restrict__ off, int64_t n, int64_t x) {

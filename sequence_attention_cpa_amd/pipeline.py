@@ -85,8 +85,7 @@ class SharePipeline:
                 rope(K, self.pos_glob, self.rope_base, self.rope_pairing, out=self.Krot)
                 Q, K = self.Qrot, self.Krot
             self._inputs = (Q, K, V)
-            share_forward(Q, K, V, self.pos, N, self.causal, self.scale, lo, hi, out=self.O,
-                          lse=self.lse)
+            share_forward(Q, K, V, N, self.causal, self.scale, lo, hi, out=self.O, lse=self.lse)
             return self.O, self.lse
         if self.rope_base is None:
             zigzag_permute(K, self.pos, N, out=self.Kr)
@@ -129,8 +128,8 @@ class SharePipeline:
             Q, K, V = self._inputs
             self.dK.zero_()
             self.dV.zero_()
-            share_backward(Q, K, V, self.pos, self.O, dO, self.lse, N, self.causal, self.dK,
-                           self.dV, self.scale, lo, hi, dQ=self.dQ, delta=self.delta)
+            share_backward(Q, K, V, self.O, dO, self.lse, N, self.causal, self.dK, self.dV,
+                           self.scale, lo, hi, dQ=self.dQ, delta=self.delta)
             return self.dQ, self.dK, self.dV
         if not hasattr(self, "dOr"):
             self.dOr = torch.empty_like(self.Qr)

@@ -23,11 +23,15 @@ F32_RTOL, F32_ATOL = 1e-5, 1e-6
 # the matrix products, whose sums are fp32, so every gradient entry carries an
 # error of a small multiple of 2^-9 times the size of its terms.  Checked
 # against the largest entry of the reference gradient (entries near zero
-# carry the same absolute error as large ones): max |d| <= 2e-2 max|ref| and
-# ||d||_2 <= 1e-2 ||ref||_2.  fp32 inputs: |d| <= 1e-5 |ref| + 1e-5 max|ref|
+# carry the same absolute error as large ones), norm-wise, and on the mean:
+# max |d| <= 7e-3 max|ref|, ||d||_2 <= 5e-3 ||ref||_2, mean |d| <= 5e-3
+# mean |ref|.  The kernels measure at most 3.6e-3 and 2.3e-3 on the first
+# two over every backward test (large logits included): the gates sit at
+# about twice that.  fp32 inputs: |d| <= 1e-5 |ref| + 1e-5 max|ref|
 # (dS = P (dP - delta) cancels, so a purely relative bound is too tight).
-GRAD_BF16_MAX_REL = 2e-2
-GRAD_BF16_NORM_REL = 1e-2
+GRAD_BF16_MAX_REL = 7e-3
+GRAD_BF16_NORM_REL = 5e-3
+GRAD_BF16_MEAN_REL = 5e-3
 GRAD_F32_RTOL = 1e-5
 GRAD_F32_ATOL_REL = 1e-5
 
@@ -38,8 +42,12 @@ def assert_grad_close(got, ref, bf16, what=""):
     if bf16:
         mx = float(d.max()) / max(scale, 1e-30) if d.size else 0.0
         nrm = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)) if d.size else 0.0
+        mean = float(d.mean() / max(float(np.abs(ref).mean()), 1e-30)) if d.size else 0.0
+        print(f"grad {what}: max-rel {mx:.3e} norm-rel {nrm:.3e} mean-rel {mean:.3e}",
+              flush=True)
         assert mx <= GRAD_BF16_MAX_REL, f"{what}: max |d| = {mx:.3e} of max|ref| > {GRAD_BF16_MAX_REL}"
         assert nrm <= GRAD_BF16_NORM_REL, f"{what}: norm-wise {nrm:.3e} > {GRAD_BF16_NORM_REL}"
+        assert mean <= GRAD_BF16_MEAN_REL, f"{what}: mean-wise {mean:.3e} > {GRAD_BF16_MEAN_REL}"
         return mx, nrm
     bound = GRAD_F32_RTOL * np.abs(ref) + GRAD_F32_ATOL_REL * scale
     worst = float((d / np.maximum(bound, 1e-300)).max()) if d.size else 0.0

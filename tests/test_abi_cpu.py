@@ -19,10 +19,14 @@ from sequence_attention_cpa_amd import _lib
 HEADER = os.path.join(ROOT, "include", "cpattn.h")
 
 
-def header_functions():
+def header_text():
+    """The header's declarations, comments removed."""
     src = open(HEADER, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(cpa_[a-z_]+)\s*\(", src)))
+    return re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+
+
+def header_functions():
+    return sorted(set(re.findall(r"\b(cpa_[a-z_]+)\s*\(", header_text())))
 
 
 @pytest.fixture(scope="module")
@@ -428,10 +432,10 @@ def test_rank_backward_rejects(lib, kw, status):
 
 
 def _share(lib, **kw):
-    a = dict(Q=P, K=P, V=P, pos=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128, N=4, lo=0, hi=4,
+    a = dict(Q=P, K=P, V=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128, N=4, lo=0, hi=4,
              causal=1, scale=0.0, O=P, lse=P, stream=None)
     a.update(kw)
-    return lib.cpa_share_forward(a["Q"], a["K"], a["V"], a["pos"], a["dt"], a["B"], a["H"], a["L"],
+    return lib.cpa_share_forward(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["H"], a["L"],
                                  a["D"], a["N"], a["lo"], a["hi"], a["causal"], a["scale"],
                                  a["O"], a["lse"], a["stream"])
 
@@ -445,7 +449,7 @@ def _share(lib, **kw):
     (dict(dt=6), _lib.CPA_EDTYPE),
     (dict(N=0), _lib.CPA_EINVAL),
     (dict(lo=2, hi=1), _lib.CPA_EINVAL),
-    (dict(pos=None), _lib.CPA_EINVAL),
+    (dict(V=None), _lib.CPA_EINVAL),
     (dict(B=2, H=32768), _lib.CPA_ESHAPE),
     (dict(L=1 << 30, H=64), _lib.CPA_ESHAPE),        # 2^28 rows per rank x 64 heads
     (dict(O=P + 4), _lib.CPA_EINVAL),
@@ -456,10 +460,10 @@ def test_share_forward_rejects(lib, kw, status):
 
 
 def _share_bwd(lib, **kw):
-    a = dict(Q=P, K=P, V=P, pos=P, O=P, dO=P, lse=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128,
+    a = dict(Q=P, K=P, V=P, O=P, dO=P, lse=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128,
              N=4, lo=0, hi=4, causal=1, scale=0.0, dQ=P, dK=P, dV=P, delta=P, stream=None)
     a.update(kw)
-    return lib.cpa_share_backward(a["Q"], a["K"], a["V"], a["pos"], a["O"], a["dO"], a["lse"],
+    return lib.cpa_share_backward(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["lse"],
                                   a["dt"], a["B"], a["H"], a["L"], a["D"], a["N"], a["lo"],
                                   a["hi"], a["causal"], a["scale"], a["dQ"], a["dK"], a["dV"],
                                   a["delta"], a["stream"])
@@ -497,11 +501,11 @@ def test_binding_rejects_mismatched_tensors():
     Q = torch.zeros(B, H, L, D, dtype=bf)
     pos = torch.zeros(N, Lr, dtype=i64)
     cases = [
-        (lambda: cpa.share_forward(Q, torch.zeros(B, H, L - 64, D, dtype=bf), Q, pos, N, True),
+        (lambda: cpa.share_forward(Q, torch.zeros(B, H, L - 64, D, dtype=bf), Q, N, True),
          _lib.CPA_ESHAPE),
-        (lambda: cpa.share_forward(Q, torch.zeros(B, H, L, D, dtype=f32), Q, pos, N, True),
+        (lambda: cpa.share_forward(Q, torch.zeros(B, H, L, D, dtype=f32), Q, N, True),
          _lib.CPA_EDTYPE),
-        (lambda: cpa.share_forward(Q, Q, Q, pos, N, True, lse=torch.zeros(B, H, L - 1)),
+        (lambda: cpa.share_forward(Q, Q, Q, N, True, lse=torch.zeros(B, H, L - 1)),
          _lib.CPA_ESHAPE),
         (lambda: cpa.partial(Q[:, :, :Lr].contiguous(), Q, Q, pos[0], pos[1], True),
          _lib.CPA_ESHAPE),
@@ -514,7 +518,7 @@ def test_binding_rejects_mismatched_tensors():
         (lambda: cpa.zigzag_permute(Q, pos, N, out=torch.zeros(N, B, H, Lr, D, dtype=f32)),
          _lib.CPA_EDTYPE),
         (lambda: cpa.rope(Q, torch.zeros(L - 1, dtype=i64)), _lib.CPA_ESHAPE),
-        (lambda: cpa.share_backward(Q, Q, Q, pos, torch.zeros(B, H, L, D), Q,
+        (lambda: cpa.share_backward(Q, Q, Q, torch.zeros(B, H, L, D), Q,
                                     torch.zeros(B, H, L), N, True, torch.zeros(B, H, L, D),
                                     torch.zeros(B, H, L, D, dtype=bf)), _lib.CPA_EDTYPE),
     ]
@@ -522,6 +526,52 @@ def test_binding_rejects_mismatched_tensors():
         with pytest.raises(cpa.CpaError) as e:
             call()
         assert e.value.status == status, str(e.value)
+
+
+def test_inverse_permute_rejects_a_source_of_the_wrong_rank_count():
+    """The inverse permute reads rank_hi - rank_lo slices of its source: a
+    source holding another number of ranks is refused on the host (these CPU
+    tensors never reach the GPU check), so the kernel cannot read past it."""
+    import torch
+    B, H, L, N, D = 1, 2, 256, 4, 64
+    pos = torch.zeros(N, L // N, dtype=torch.int64)
+    one_rank = torch.zeros(1, B, H, L // N, D, dtype=torch.bfloat16)
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.zigzag_permute(one_rank, pos, N, inverse=True)  # default range: all N ranks
+    assert e.value.status == _lib.CPA_ESHAPE and "src" in str(e.value)
+    with pytest.raises(cpa.CpaError) as e:  # lse-shaped source, 3 ranks for a 2-rank range
+        cpa.zigzag_permute(torch.zeros(3, B, H, L // N), pos, N, inverse=True, rank_lo=1,
+                           rank_hi=3)
+    assert e.value.status == _lib.CPA_ESHAPE
+
+
+def test_share_calls_take_no_position_table():
+    """The global-layout calls address rows through the zigzag closed form and
+    take their causal bounds from the same closed form, so they take no table
+    that could disagree with it (a contiguous table once gave wrong results
+    with CPA_OK)."""
+    import inspect
+    decl = header_text()
+    for name in ("cpa_share_forward", "cpa_share_backward"):
+        i = decl.index(name + "(")
+        params = decl[i:decl.index(")", i)]
+        assert "pos" not in params and "int64_t" in params, params
+    for fn in (cpa.share_forward, cpa.share_backward):
+        assert "pos_all" not in inspect.signature(fn).parameters
+
+
+def test_debug_range_check_of_permute_tables(monkeypatch):
+    """Debug mode refuses a permute table with an entry outside [0, L) before
+    anything reaches the library (checked here on CPU tensors)."""
+    import torch
+    import sequence_attention_cpa_amd as m
+    monkeypatch.setattr(m, "_debug_offsets", True)
+    with pytest.raises(cpa.CpaError) as e:
+        m._debug_range(torch.tensor([[0, 5], [6, 64]], dtype=torch.int64), 64)
+    assert e.value.status == _lib.CPA_EINVAL and "max 64" in str(e.value)
+    with pytest.raises(cpa.CpaError):
+        m._debug_range(torch.tensor([[-1, 5]], dtype=torch.int64), 64)
+    m._debug_range(torch.tensor([[0, 63]], dtype=torch.int64), 64)
 
 
 def test_error_text_is_per_thread():

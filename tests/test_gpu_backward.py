@@ -306,11 +306,11 @@ def test_share_backward_rank_subset():
     pos = cpa.zigzag_layout(L, N)
     posd = pos.to(DEV)
     Qd, Kd, Vd, dOd = (x.to(DEV) for x in (Q, K, V, dO))
-    O, lse = cpa.share_forward(Qd, Kd, Vd, posd, N, causal)
+    O, lse = cpa.share_forward(Qd, Kd, Vd, N, causal)
     dK = torch.zeros((B, H, L, D), dtype=torch.float32, device=DEV)
     dV = torch.zeros_like(dK)
     dQ = torch.full((B, H, L, D), 7.0, dtype=torch.float32, device=DEV)
-    cpa.share_backward(Qd, Kd, Vd, posd, O, dOd, lse, N, causal, dK, dV, rank_lo=1, rank_hi=3,
+    cpa.share_backward(Qd, Kd, Vd, O, dOd, lse, N, causal, dK, dV, rank_lo=1, rank_hi=3,
                        dQ=dQ)
     torch.cuda.synchronize()
     dQ, dK, dV = (x.cpu().double().numpy() for x in (dQ, dK, dV))

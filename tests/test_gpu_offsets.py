@@ -110,9 +110,11 @@ def test_debug_mode_rejects_bad_tables_before_causal_calls():
             assert e.value.status == cpa.CPA_EINVAL and "entry 100" in str(e.value)
         cpa.partial(Q, K, V, good, good, causal=True)
         with pytest.raises(cpa.CpaError) as e:
-            cpa.share_forward(Q, K, V, pos_bad, N, causal=True)
+            cpa.rank_forward_fused(1, N, Q[:, :, :L // N].contiguous(),
+                                   torch.stack([K[:, :, :L // N], K[:, :, L // N:]]).contiguous(),
+                                   torch.stack([V[:, :, :L // N], V[:, :, L // N:]]).contiguous(),
+                                   pos_bad, causal=True)
         assert "pos_all" in str(e.value) and "row 1, entry 70" in str(e.value)
-        cpa.share_forward(Q, K, V, pos, N, causal=True)
         torch.cuda.synchronize()
     finally:
         cpa.debug_offsets(False)
@@ -146,8 +148,6 @@ def test_debug_mode_covers_the_ring_and_backward_calls():
                                                          bad_off, True, dQi, dKi, dVi),
         "rank_backward": lambda: cpa.rank_backward(0, N, Qi, Kr, Vr, bad_pos, Oi, dOi, lsei, True,
                                                    dKr, dVr),
-        "share_backward": lambda: cpa.share_backward(Q, K, V, bad_pos, O, dO, lse, N, True, dK,
-                                                     dV, dQ=dQ),
     }
     cpa.debug_offsets(True)
     try:

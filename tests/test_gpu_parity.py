@@ -433,7 +433,7 @@ def test_share_forward_rank_subset_leaves_other_rows():
     pos = cpa.zigzag_layout(L, N)
     O = torch.full((B, H, L, D), 7.0, device=DEV)
     lse = torch.full((B, H, L), 7.0, device=DEV)
-    cpa.share_forward(Q, K, V, pos.to(DEV), N, True, rank_lo=1, rank_hi=3, out=O, lse=lse)
+    cpa.share_forward(Q, K, V, N, True, rank_lo=1, rank_hi=3, out=O, lse=lse)
     torch.cuda.synchronize()
     mine = np.concatenate([pos[1].numpy(), pos[2].numpy()])
     other = np.setdiff1d(np.arange(L), mine)
