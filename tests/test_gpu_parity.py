@@ -96,7 +96,7 @@ def test_partial_mfma_bf16(case):
 
 
 def test_partial_zigzag_small_chunks_bf16():
-    """Chunks of 8 tokens (shorter than a 64-key tile): every K tile mixes
+    """Chunks of 8 tokens (shorter than a 32-key tile): every K tile mixes
     visible and hidden keys of several chunks, for every (i, j) pair."""
     B, H, L, N, D = 1, 2, 256, 16, 128
     pos = cpa_oracle.zigzag_layout(L, N)

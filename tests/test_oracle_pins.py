@@ -250,16 +250,13 @@ def check_sampled_rows(orc):
 
 # ------------------------------------------------------------------ rope pins
 
-def _page_sinusoid(p, d):
-    """The sinusoidal table of "Tensor并行与算子拆分" (model code,
-    PositionalEncoding), written out with the page's own steps: divisor
-    exp(2k * (-ln 10000 / d)); even columns sin(p * div), odd columns cos."""
-    row = [0.0] * d
-    for k2 in range(0, d, 2):
-        div = math.exp(k2 * (-math.log(10000.0) / d))
-        row[k2] = math.sin(p * div)
-        row[k2 + 1] = math.cos(p * div)
-    return row
+def _sinusoid_table(p, d):
+    """Row p of the sinusoidal position table that "Tensor并行与算子拆分"
+    (model code, PositionalEncoding) builds, from its definition: pair k
+    (columns 2k and 2k+1) holds the sine and cosine of the angle p * theta_k,
+    with the frequency theta_k = 10000^(-2k/d)."""
+    angles = [p * 10000.0 ** (-2.0 * k / d) for k in range(d // 2)]
+    return [f(a) for a in angles for f in (math.sin, math.cos)]
 
 
 def check_rope_sinusoid_table(orc):
@@ -268,7 +265,7 @@ def check_rope_sinusoid_table(orc):
     the pairing and the direction of the rotation."""
     for d in (2, 8, 16, 128):
         positions = np.array([0, 1, 2, 7, 100, 4095, 131071], dtype=np.int64)
-        table = np.array([_page_sinusoid(int(p), d) for p in positions])
+        table = np.array([_sinusoid_table(int(p), d) for p in positions])
         for pairing in (orc.ROPE_INTERLEAVED, orc.ROPE_HALF):
             x = np.zeros((len(positions), d))
             first = np.arange(0, d, 2) if pairing == orc.ROPE_INTERLEAVED else np.arange(d // 2)
