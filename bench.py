@@ -18,9 +18,14 @@ number of (query, key) pairs the rank's queries may see (key position <= query
 position), i.e. masked and skipped work is not counted.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the attention
-kernel, bf16 MFMA-bound): its useful FLOP per launch over its average launch
-duration, timed with HIP events on the launch stream.  `cpu_baseline` times
-the fp64 CPU oracle on a bounded sample of the same share's query rows.
+kernel, bf16 MFMA-bound): its useful FLOP per launch over the median duration
+of the timed steps' launches, timed with HIP events on the launch stream (in
+the default mode a step is that one launch).  `kernels` adds the other launch
+forms, the backward, the 12k workload's four ranks, and the bandwidth-bound
+kernels (merge, permute, permute+RoPE) against a plain device copy, timed at
+the 1M share's sizes so that their working sets exceed the 256 MB MALL.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+share's query rows, on every host core the process may use.
 """
 import argparse
 import hashlib
@@ -63,9 +68,23 @@ def pmc_traffic(ring):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, Q, K, V, pos_rank, seconds):
+def blas_info():
+    """numpy's BLAS as threadpoolctl reports it: vendor, library, threads."""
+    try:
+        from threadpoolctl import threadpool_info
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                return {"vendor": d.get("internal_api"), "library": os.path.basename(
+                    d.get("filepath", "")), "threads_default": d.get("num_threads")}
+    except Exception:  # pragma: no cover
+        pass
+    return None
+
+
+def cpu_baseline(w, Q, K, V, pos_rank, seconds, useful_flop):
     """The oracle, untouched, over a sample of the rank's query rows; rows are
-    independent, so host threads each take whole (head, row-block) tasks."""
+    independent, so host threads each take whole (head, row-block) tasks, one
+    BLAS thread each, on every core the process may use."""
     import numpy as np
     import torch
     from concurrent.futures import ThreadPoolExecutor
@@ -76,7 +95,7 @@ def cpu_baseline(w, Q, K, V, pos_rank, seconds):
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = max(1, len(os.sched_getaffinity(0)))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     K64 = {bh: K[bh].to(torch.float64).numpy() for bh in heads}
     V64 = {bh: V[bh].to(torch.float64).numpy() for bh in heads}
@@ -84,7 +103,7 @@ def cpu_baseline(w, Q, K, V, pos_rank, seconds):
     block = 16
     # sample row blocks from the whole share, timing until the budget is spent
     tasks = []
-    for _ in range(4096):
+    for _ in range(8192):
         bh = heads[int(rng.integers(len(heads)))]
         t0 = int(rng.integers(0, len(pos_rank) - block + 1))
         tasks.append((bh, pos_rank[t0:t0 + block]))
@@ -109,10 +128,89 @@ def cpu_baseline(w, Q, K, V, pos_rank, seconds):
             i += len(batch)
     el = time.perf_counter() - t_start
     flops = 4.0 * w.D * pairs
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done_rows} query rows of rank share ({block}-row blocks, random heads "
-                      f"and positions, seed 0), fp64 numpy, {el:.1f} s, BLAS 1 thread/worker",
-            "seconds": round(el, 2)}
+    value = flops / el / 1e12
+    share_rows = w.B * w.H * len(pos_rank)
+    return {"value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_rows} of the share's {share_rows} query rows ({block}-row blocks, "
+                      f"random heads and positions, seed 0), fp64 numpy, {el:.1f} s, "
+                      f"{cores} worker threads with 1 BLAS thread each",
+            "seconds": round(el, 2), "rows": done_rows,
+            "seconds_per_row": round(el / max(done_rows, 1), 6), "blas": blas_info(),
+            "extrapolated_full_share_seconds": round(useful_flop / (value * 1e12), 1),
+            "extrapolation": "the share's useful FLOP at the sampled rate (extrapolated, "
+                             "not measured)"}
+
+
+def zig_pairs(L, N, ranks):
+    """Visible (query, key) pairs of the given ranks' rings under the zigzag
+    layout (closed form 2N C^2 + C per head and rank, C = L / 2N)."""
+    C = L // (2 * N)
+    return len(ranks) * (2 * N * C * C + C)
+
+
+def small_share(cpa, torch, dev, timed, reps):
+    """The 12k workload's shape (B 1, H 32, D 128, L 12288, CP 4), all four
+    ranks' rings in one cpa_share_forward call, on device-generated bf16
+    N(0,1) inputs."""
+    import numpy as np
+    B, H, L, D, N = 1, 32, 12288, 128, 4
+    g = torch.Generator(device=dev).manual_seed(12)
+    Q, K, V = (torch.randn((B, H, L, D), generator=g, device=dev, dtype=torch.float32)
+               .to(torch.bfloat16) for _ in range(3))
+    O = torch.empty((B, H, L, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    fn = lambda: cpa.share_forward(Q, K, V, N, True, out=O, lse=lse)  # noqa: E731
+    fn()
+    evs = timed(fn, reps)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    flop = 4.0 * D * B * H * zig_pairs(L, N, range(N))
+    med = float(np.median(ms))
+    return {"workload": "12k: B=1 H=32 D=128 L=12288 CP=4, all 4 ranks, one cpa_share_forward",
+            "ms_median": round(med, 4), "ms_min": round(float(ms.min()), 4),
+            "TFLOP/s": round(flop / (med * 1e-3) / 1e12, 2), "useful_flop": flop}
+
+
+def bandwidth(cpa, torch, dev, timed, reps):
+    """HBM-bound kernels at the 1M share's sizes (B 1, H 4, D 128, L 2^20,
+    CP 8: every working set 0.8-2 GiB, well past the 256 MB MALL), against a
+    plain device-to-device copy of the permute's size."""
+    import numpy as np
+    B, H, L, D, N = 1, 4, 1 << 20, 128, 8
+    Lr = L // N
+    rows = B * H * Lr
+    out = {"sizes": "1M share: B=1 H=4 D=128 L=1048576 CP=8", "mall_free": True,
+           "peak_GB/s": PEAK_HBM_GBS}
+
+    def rate(name, fn, nbytes):
+        fn()
+        evs = timed(fn, reps)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms_median": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                     "frac_of_peak": round(gbs / PEAK_HBM_GBS, 3)}
+
+    f32 = dict(dtype=torch.float32, device=dev)
+    Oa, On = torch.randn((rows, D), **f32), torch.randn((rows, D), **f32)
+    la, ln = torch.randn((rows,), **f32), torch.randn((rows,), **f32)
+    # read both partials, write the accumulator (O and lse)
+    rate("merge", lambda: cpa.merge(Oa, la, On, ln), rows * (D + 1) * 4 * 3)
+    del Oa, On, la, ln
+    K = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=dev).normal_()
+    Kr = torch.empty((N, B, H, Lr, D), dtype=torch.bfloat16, device=dev)
+    pos = cpa.zigzag_layout(L, N).to(dev)
+    nb = 2 * K.numel() * K.element_size()  # read K once, write it once
+    rate("permute_K", lambda: cpa.zigzag_permute(K, pos, N, out=Kr), nb)
+    rate("permute_rope_K", lambda: cpa.zigzag_permute_rope(K, pos, N, 10000.0, out=Kr), nb)
+    Kc = torch.empty_like(K)
+    rate("device_copy_same_bytes", lambda: Kc.copy_(K), nb)
+    c = out["device_copy_same_bytes"]["GB/s"]
+    for name in ("merge", "permute_K", "permute_rope_K"):
+        out[name]["frac_of_copy"] = round(out[name]["GB/s"] / c, 3)
+    del K, Kr, Kc
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -129,6 +227,9 @@ def main():
                     help="also time the rank's ring backward (reported under kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--extra", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the 12k workload's ranks and the bandwidth-bound kernels at "
+                         "1M sizes (reported under kernels)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -254,9 +355,6 @@ def main():
             part_evs += [(j, e) for e in timed(lambda: cpa.partial(
                 rk.Qr[0], rk.Kr[j], rk.Vr[j], pos_d[rank], pos_d[j], w.causal, out=tO,
                 lse=tl), 1)]
-    mevs = timed(lambda: cpa.merge(rk.Or[0], rk.lser[0], tO, tl), reps)
-    pevs = timed(lambda: cpa.zigzag_permute(K, pos_d, w.N, out=rk.Kr), reps)
-    rope_evs = timed(lambda: cpa.zigzag_permute_rope(K, pos_d, w.N, 10000.0, out=rk.Kr), reps)
     # Ring backward of the same rank (delta + dQ pass + dK/dV pass), after a
     # forward step so that O and lse are the ring's: on global-order data
     # (cpa_share_backward, the pipeline's backward in the default mode) and on
@@ -294,28 +392,27 @@ def main():
         return {"median": round(float(np.median(x)), 4), "min": round(float(np.min(x)), 4),
                 "p90": round(float(np.percentile(x, 90)), 4)}
     if args.ring == "global":
+        # a step is this one launch: the timed steps' own launch durations
         dom_kernel = (f"attn_fwd_kernel<{w.D}, global layout> (one launch, {w.N} K/V "
                       "blocks)")
-        dom_ms = float(g_ms.mean())
+        dom_ms = float(np.median(step_ms))
+        dom_src = f"median of the {args.steps} timed steps (one launch each)"
         dom_flop = useful
     elif fused:
         dom_kernel = f"attn_fwd_kernel<{w.D}> (one launch, {w.N} K/V blocks)"
-        dom_ms = float(f_ms.mean())
+        dom_ms = float(np.median(f_ms))
+        dom_src = f"median of {len(f_ms)} launches after the timed steps"
         dom_flop = useful
     else:
         dom_kernel = f"attn_fwd_kernel<{w.D}> (one K/V block)"
-        dom_ms = p_avg_ms
+        dom_ms = float(np.median(p_ms))
+        dom_src = f"median of {len(p_ms)} partial launches after the timed steps"
         dom_flop = float(p_flops.mean())
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
-    m_ms = float(np.mean([a.elapsed_time(b) for a, b in mevs]))
-    m_bytes = w.B * w.H * Lr * (w.D + 1) * 4 * 3  # read acc + new, write acc (O and lse)
-    perm_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
-    perm_bytes = 2 * K.numel() * K.element_size()
-    rope_ms = float(np.mean([a.elapsed_time(b) for a, b in rope_evs]))
     def bwd_report(evs):
         if not evs:
             return None
-        b_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        b_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
         b_flop = 2.0 * useful  # dV, dP, dQ, dK: 4 products of 2*D per visible pair
         return {"ms": round(b_ms, 4), "TFLOP/s": round(b_flop / (b_ms * 1e-3) / 1e12, 2),
                 "useful_flop": b_flop}
@@ -335,6 +432,12 @@ def main():
                    "zigzag_pairs": [sum(pairs), sum(
                        causal_pairs(pos[w.N - 1], pos[j]) for j in range(w.N))],
                    "zigzag_step_efficiency": round((z0 + zl) / 2 / max(z0, zl), 3)}
+
+    # After the share's own kernels: the 12k shape, then the HBM-bound kernels
+    # at 1M sizes (their buffers are freed before the CPU baseline).
+    del rk, tO, tl
+    small = small_share(cpa, torch, dev, timed, reps) if args.extra else None
+    bw = bandwidth(cpa, torch, dev, timed, reps) if args.extra else None
 
     value = useful / (ms_step * 1e-3) / 1e12
     out = {
@@ -359,7 +462,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": pmc_traffic(args.ring), "kernel": dom_kernel,
-                     "avg_launch_ms": round(dom_ms, 4), "useful_flop_per_launch": dom_flop},
+                     "launch_ms": round(dom_ms, 4), "launch_ms_from": dom_src,
+                     "useful_flop_per_launch": dom_flop},
         "kernels": {
             "ring": args.ring,
             "global_ring_ms_stats": stats(g_ms) if g_ms is not None else None,
@@ -369,14 +473,8 @@ def main():
                                          if o_ms is not None else None),
             "partial_ms": [round(float(x), 4) for x in p_ms[: w.N]],
             "partial_TFLOP/s": round(float(p_flops.mean()) / (p_avg_ms * 1e-3) / 1e12, 2),
-            "merge": {"ms": round(m_ms, 4), "GB/s": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
-                      "bytes": m_bytes},
-            "permute_K": {"ms": round(perm_ms, 4),
-                          "GB/s": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
-                          "bytes": perm_bytes},
-            "permute_rope_K": {"ms": round(rope_ms, 4),
-                               "GB/s": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
-                               "bytes": perm_bytes},
+            "small_share_12k": small,
+            "bandwidth": bw,
             "ms_per_step_events": round(ms_step_ev, 4),
             "step_ms_stats": stats(step_ms),
             "balance_first_last_rank": balance,
@@ -386,7 +484,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu and rank == 0:
-        out["cpu_baseline"] = cpu_baseline(w, Qh, Kh, Vh, pos[rank], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, Qh, Kh, Vh, pos[rank], args.cpu_seconds, useful)
     print(json.dumps(out), flush=True)
 
 

@@ -184,7 +184,8 @@ cpa_status cpa_rank_forward_fused(int32_t i, int32_t N, const void *Q_i, const v
  *              rows are written, the others are left untouched
  *   causal, scale   as for cpa_partial
  * bf16 with D = 64 or 128 and C a multiple of 32 (CPA_EUNSUPPORTED otherwise;
- * use the permute + cpa_rank_forward_fused path).  One launch per rank.
+ * use the permute + cpa_rank_forward_fused path).  One launch for all the
+ * selected ranks.
  */
 cpa_status cpa_share_forward(const void *Q, const void *K, const void *V, cpa_dtype dt, int32_t B,
                              int32_t H, int64_t L, int32_t D, int32_t N, int32_t rank_lo,

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ O,
     float* __restrict__ lse, int BH, int Lq, int Lk, int64_t kv_stride, int64_t koff_stride,
-    int nblk, int first, int causal, float c_log2, int n_qtiles) {
+    int nblk, int rank0, int nranks, int causal, float c_log2, int n_qtiles) {
   using G = Geo<D>;
   constexpr int TB = G::TILE_BYTES;
   constexpr int RB = G::ROW_BYTES;
@@ -146,8 +146,12 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
   const int lr = lane & 31;
+  // Workgroups: heads fastest, then the launch's ranks, then query tiles,
+  // longest first (ranks' tiles of one index carry the same zigzag work).
   const int bh = blockIdx.x % BH;
-  const int qt = n_qtiles - 1 - blockIdx.x / BH;
+  const int rest = blockIdx.x / BH;
+  const int first = rank0 + rest % nranks;  // this workgroup's rank
+  const int qt = n_qtiles - 1 - rest / nranks;
   const int q0 = qt * BM;                         // first local row of the workgroup
   const int qlast = min(q0 + BM, Lq) - 1;         // its last valid row
   const int w0 = q0 + wv * 32;                    // first local row of this wave
@@ -571,19 +575,21 @@ template <bool GL, int W>
 hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int64_t* q_off,
                          const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
                          int64_t Lk, int64_t kv_stride, int64_t koff_stride, int nblk, int first,
-                         int D, bool causal, float scale, hipStream_t stream) {
+                         int nranks, int D, bool causal, float scale, hipStream_t stream) {
   const int n_qtiles = (int)((Lq + BM - 1) / BM);
-  const dim3 grid((unsigned)(n_qtiles * BH));
+  const dim3 grid((unsigned)((int64_t)n_qtiles * BH * nranks));
   const float c_log2 = scale * LOG2E;
   if (D == 128) {
     hipLaunchKernelGGL((attn_fwd_kernel<128, GL, W>), grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
-                       BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0,
+                       BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, nranks,
+                       causal ? 1 : 0,
                        c_log2, n_qtiles);
   } else {
     hipLaunchKernelGGL((attn_fwd_kernel<64, GL, W>), grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
-                       BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0,
+                       BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, nranks,
+                       causal ? 1 : 0,
                        c_log2, n_qtiles);
   }
   return hipGetLastError();
@@ -594,8 +600,8 @@ hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int6
 hipError_t launch_partial_mfma(const void* Q, const void* K, const void* V, const int64_t* q_off,
                                const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
                                int64_t Lk, int D, bool causal, float scale, hipStream_t stream) {
-  return launch_blocks<false, 4>(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, 0, 0, 1, 0, D, causal,
-                                 scale, stream);
+  return launch_blocks<false, 4>(Q, K, V, q_off, k_off, O, lse, BH, Lq, Lk, 0, 0, 1, 0, 1, D,
+                                 causal, scale, stream);
 }
 
 hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_all,
@@ -603,14 +609,14 @@ hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_al
                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
                             hipStream_t stream) {
   return launch_blocks<false, 4>(Q_i, K_all, V_all, q_off, pos_all, O, lse, BH, Lr, Lr,
-                                 (int64_t)BH * Lr * D, Lr, N, i, D, causal, scale, stream);
+                                 (int64_t)BH * Lr * D, Lr, N, i, 1, D, causal, scale, stream);
 }
 
 hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, float* O, float* lse,
-                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
-                             hipStream_t stream) {
-  return launch_blocks<true, 8>(Q, K, V, nullptr, nullptr, O, lse, BH, Lr, Lr, 0, 0, N, i, D,
-                                causal, scale, stream);
+                             int BH, int64_t Lr, int N, int rank_lo, int nranks, int D,
+                             bool causal, float scale, hipStream_t stream) {
+  return launch_blocks<true, 8>(Q, K, V, nullptr, nullptr, O, lse, BH, Lr, Lr, 0, 0, N, rank_lo,
+                                nranks, D, causal, scale, stream);
 }
 
 }  // namespace cpa

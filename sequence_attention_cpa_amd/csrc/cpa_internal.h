@@ -28,13 +28,14 @@ hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_al
                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
                             hipStream_t stream);
 
-// Rank i's whole ring in one launch on global-order data: Q, K, V [BH, N*Lr, D]
-// and O, lse [BH, N*Lr, ...] in global token order, rank r's local row u at
-// zigzag row zig(r, u), which is also its position (the causal bounds are
-// that closed form).  Requires Lr/2 % 32 == 0; writes only rank i's rows.
+// The whole rings of ranks [rank_lo, rank_lo + nranks) in one launch on
+// global-order data: Q, K, V [BH, N*Lr, D] and O, lse [BH, N*Lr, ...] in
+// global token order, rank r's local row u at zigzag row zig(r, u), which is
+// also its position (the causal bounds are that closed form).  Requires
+// Lr/2 % 32 == 0; writes only those ranks' rows.
 hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, float* O, float* lse,
-                             int BH, int64_t Lr, int N, int i, int D, bool causal, float scale,
-                             hipStream_t stream);
+                             int BH, int64_t Lr, int N, int rank_lo, int nranks, int D,
+                             bool causal, float scale, hipStream_t stream);
 
 // Partial attention, one query row per thread, fp32 arithmetic throughout
 // (fp32 inputs, and bf16 inputs with D = 16).

@@ -438,19 +438,18 @@ cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, cpa_dt
                 (long long)L, N);
   if (Lr > ((int64_t)1 << 30)) return fail(CPA_ESHAPE, "L/N is limited to 2^30 rows");
   if ((int64_t)B * H > kMaxBH) return fail(CPA_ESHAPE, "B*H is limited to %lld", (long long)kMaxBH);
-  st = check_mfma_launch(dt, D, (int64_t)B * H, Lr, Lr, 0);
+  // one launch covers every selected rank
+  st = check_mfma_launch(dt, D, (int64_t)B * H * (rank_hi - rank_lo), Lr, Lr, 0);
   if (st != CPA_OK) return st;
   if (!Q || !K || !V || !O || !lse) return fail(CPA_EINVAL, "null pointer");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
     return fail(CPA_EINVAL, "Q, K, V and O must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(CPA_EINVAL, "lse must be 4-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
-  for (int32_t r = rank_lo; r < rank_hi; ++r) {
-    const hipError_t e = cpa::launch_share_mfma(Q, K, V, O, lse, B * H, Lr, N, r, D,
-                                                causal != 0, scale, (hipStream_t)stream);
-    if (e != hipSuccess) return from_hip(e, "global-layout ring launch");
-  }
-  return ok();
+  return from_hip(cpa::launch_share_mfma(Q, K, V, O, lse, B * H, Lr, N, rank_lo,
+                                         rank_hi - rank_lo, D, causal != 0, scale,
+                                         (hipStream_t)stream),
+                  "global-layout ring launch");
 }
 
 cpa_status cpa_backward_delta(const float* O, const void* dO, cpa_dtype dt, int64_t rows,
