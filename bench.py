@@ -250,7 +250,7 @@ def main():
     dev = "cuda:0"
     w = WORKLOADS[args.workload]
     rank = args.rank
-    Qh, Kh, Vh, _ = make_inputs(w)
+    Qh, Kh, Vh, outl = make_inputs(w)
     Q, K, V = Qh.to(dev), Kh.to(dev), Vh.to(dev)
     mfma_ok = w.dtype == "bf16" and w.D in (64, 128)
     global_ok = mfma_ok and (w.C % 32 == 0)
@@ -323,6 +323,21 @@ def main():
         share_evs = timed(lambda: cpa.share_forward(Q, K, V, w.N, w.causal,
                                                     rank_lo=rank, rank_hi=rank + 1, out=pipe.O,
                                                     lse=pipe.lse), reps)
+    # Precise weights (cpa_share_forward_precise) on the same share with the
+    # outlier rows scaled in V as well (the 128k_qkv inputs: V's outlier rows
+    # times 8, exact in bf16), next to the bf16-weight launch on those inputs.
+    qkv = None
+    if global_ok and args.extra and len(outl) and w.outlier_mult != 1.0 and not w.outlier_in_v:
+        Vx = V.clone()
+        Vx[:, :, torch.from_numpy(outl).to(dev)] *= w.outlier_mult
+        qkv = {}
+        for name, prec in (("bf16_weights", False), ("precise_weights", True)):
+            f = lambda: cpa.share_forward(Q, K, Vx, w.N, w.causal, rank_lo=rank,  # noqa: E731
+                                          rank_hi=rank + 1, out=pipe.O, lse=pipe.lse,
+                                          precise=prec)
+            f()
+            qkv[name] = timed(f, reps)
+        del Vx
     fused_evs, last_evs = [], []
     if mfma_ok:
         fused_evs = timed(lambda: cpa.rank_forward_fused(rank, w.N, rk.Qr[0], rk.Kr, rk.Vr,
@@ -409,6 +424,15 @@ def main():
         dom_src = f"median of {len(p_ms)} partial launches after the timed steps"
         dom_flop = float(p_flops.mean())
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    qkv_report = None
+    if qkv:
+        qkv_report = {"inputs": f"{w.name} share with the outlier rows scaled in V too "
+                                f"(x{w.outlier_mult:g}), rank {rank}"}
+        for name, evs in qkv.items():
+            ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+            qkv_report[name] = {"ms_median": round(ms, 4),
+                                "TFLOP/s": round(useful / (ms * 1e-3) / 1e12, 2)}
+
     def bwd_report(evs):
         if not evs:
             return None
@@ -473,6 +497,7 @@ def main():
                                          if o_ms is not None else None),
             "partial_ms": [round(float(x), 4) for x in p_ms[: w.N]],
             "partial_TFLOP/s": round(float(p_flops.mean()) / (p_avg_ms * 1e-3) / 1e12, 2),
+            "outliers_in_v": qkv_report,
             "small_share_12k": small,
             "bandwidth": bw,
             "ms_per_step_events": round(ms_step_ev, 4),

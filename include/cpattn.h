@@ -193,6 +193,23 @@ cpa_status cpa_share_forward(const void *Q, const void *K, const void *V, cpa_dt
                              void *stream);
 
 /*
+ * cpa_share_forward with precise weights, for inputs whose V rows differ
+ * widely in size.  The softmax weights multiply V in the output sum
+ * ("Tensor并行与算子拆分", 注意力的并行化优化); cpa_share_forward rounds them to
+ * bf16 first, which bounds O's error by V's largest rows times the bf16
+ * rounding.  Here each weight p is split into hi = bf16(p) and
+ * lo = bf16(p - hi), both multiply V on the matrix cores, and O is divided
+ * by the fp32 sum of the weights: O's error no longer grows with V's scale.
+ * The matrix cores do 24 instead of 18 products per tile (D = 128), so the
+ * launch takes longer.  Arguments, layout, outputs and errors as for
+ * cpa_share_forward.
+ */
+cpa_status cpa_share_forward_precise(const void *Q, const void *K, const void *V, cpa_dtype dt,
+                                     int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+                                     int32_t rank_lo, int32_t rank_hi, int32_t causal,
+                                     float scale, float *O, float *lse, void *stream);
+
+/*
  * Permutation between global order and rank-major zigzag order, for ranks
  * [rank_lo, rank_hi) (the data-pipeline step of "序列与上下文并行", 工程实践:
  * each rank's data must follow the CP layout).

@@ -250,11 +250,12 @@ def rank_forward_fused(i: int, N: int, Q_i, K_all, V_all, pos_all, causal: bool,
 
 
 def share_forward(Q, K, V, N: int, causal: bool, scale: float = 0.0, rank_lo: int = 0,
-                  rank_hi: int | None = None, out=None, lse=None):
+                  rank_hi: int | None = None, out=None, lse=None, precise: bool = False):
     """Rings of ranks [rank_lo, rank_hi) on global-order Q/K/V [B,H,L,D] (bf16):
     O [B,H,L,D] and lse [B,H,L] float32 in global order, the selected ranks'
     rows written (the zigzag permute folded into the kernel's addressing, a
-    token's position its global index: no position table)."""
+    token's position its global index: no position table).  precise=True
+    calls cpa_share_forward_precise (softmax weights as a bf16 pair)."""
     torch = _torch()
     rank_hi = N if rank_hi is None else rank_hi
     B, H, L, D = Q.shape
@@ -268,9 +269,9 @@ def share_forward(Q, K, V, N: int, causal: bool, scale: float = 0.0, rank_lo: in
     _expect(out, (B, H, L, D), f32, "out")
     _expect(lse, (B, H, L), f32, "lse")
     _need_gpu(Q, K, V, out, lse)
-    check(load().cpa_share_forward(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, L, D, N,
-                                   rank_lo, rank_hi, int(bool(causal)), float(scale), _ptr(out),
-                                   _ptr(lse), _stream(Q)))
+    fn = load().cpa_share_forward_precise if precise else load().cpa_share_forward
+    check(fn(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, L, D, N, rank_lo, rank_hi,
+             int(bool(causal)), float(scale), _ptr(out), _ptr(lse), _stream(Q)))
     return out, lse
 
 

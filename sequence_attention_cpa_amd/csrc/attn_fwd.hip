@@ -55,6 +55,12 @@
 //    closed form, so no position table is read.
 //  * Workgroups are issued longest-first (last query tiles first), heads
 //    fastest, so each XCD keeps working on the same heads' K/V in its L2.
+//  * Precise weights (PP, global layout only, opt-in): each P is split into
+//    hi = bf16(P) and lo = bf16(P - hi), and the PV product runs twice per V
+//    fragment, once on each part.  hi + lo carries P to a relative 2^-16, so
+//    the bf16 rounding of P no longer limits O, and O is divided by the fp32
+//    sum instead (no matrix-core row sums).  It costs 8 MFMAs per tile
+//    (24 instead of 18 at D = 128) and about 40 VALU instructions.
 #include "cpa_internal.h"
 #include "mfma_tile.h"
 
@@ -121,7 +127,7 @@ __device__ __forceinline__ int lds_slot(int r, int c) {
 // token order; rank r's local row u is global row zig(r, u), which is also
 // its position.  Lq/2 is a multiple of 32, so every 32-row tile is
 // contiguous in memory and lies in one chunk.
-template <int D, bool GL, int W>
+template <int D, bool GL, int W, bool PP>
 __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ O,
@@ -262,6 +268,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   f32x16 s[2];            // scores of two tiles (S^T layout), by tile parity
   bf16x8 pf[2][2];        // bf16 P of two tiles, by tile parity, key halves
+  bf16x8 pl[2][2];        // PP: the residuals P - hi, same indexing
   float m2 = M_INIT;      // exponent reference (log2 units): an integer after the first tile
   float L32 = 0.f;        // this lane's share of the fp32 row sum (gives lse)
   // Row sums of the bf16 P (normalise O), accumulated on the matrix core as
@@ -272,12 +279,24 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   float ts32;             // the lane's fp32 tile sum, added once the tile passed its check
   const f32x16 zero16 = {};
 
+  // bf16 residuals of a packed pair: bf16(p0 - hi0), bf16(p1 - hi1), where
+  // w holds hi0 in its low half and hi1 in its high half.  p - hi is exact
+  // in fp32.
+  auto residual = [](float p0, float p1, uint32_t w) __attribute__((always_inline)) -> uint32_t {
+    const float h0 = __builtin_bit_cast(float, w << 16);
+    const float h1 = __builtin_bit_cast(float, w & 0xffff0000u);
+    return cvt_pk_bf16(p0 - h0, p1 - h1);
+  };
+  auto pack = [](const uint32_t* w, int h) __attribute__((always_inline)) -> bf16x8 {
+    const u32x4 q4 = {w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+    return __builtin_bit_cast(bf16x8, q4);
+  };
   // Weights of one tile at the current reference: P packed to bf16 for the
-  // PV product and the lane's fp32 sum.
-  auto softmax = [&](const f32x16& sj, bf16x8 (&pj)[2], float& t32)
+  // PV product (PP: and its residuals) and the lane's fp32 sum.
+  auto softmax = [&](const f32x16& sj, bf16x8 (&pj)[2], bf16x8 (&pjl)[2], float& t32)
                      __attribute__((always_inline)) {
     float a[4];
-    uint32_t pw[8];
+    uint32_t pw[8], lw[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sj[r], c_log2, -m2));
@@ -290,18 +309,19 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         a[(r + 1) & 3] += p1;
       }
       pw[r >> 1] = cvt_pk_bf16(p0, p1);
+      if constexpr (PP) lw[r >> 1] = residual(p0, p1, pw[r >> 1]);
     }
     t32 = (a[0] + a[1]) + (a[2] + a[3]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4 q4 = {pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]};
-      pj[h] = __builtin_bit_cast(bf16x8, q4);
+      pj[h] = pack(pw, h);
+      if constexpr (PP) pjl[h] = pack(lw, h);
     }
   };
   // The tile's exact row max raises the reference (to its ceiling) when it
   // is above it; O and the running sums are rescaled by the power of two,
   // then the tile's weights are recomputed.
-  auto reraise = [&](const f32x16& sj, bf16x8 (&pj)[2], float& t32)
+  auto reraise = [&](const f32x16& sj, bf16x8 (&pj)[2], bf16x8 (&pjl)[2], float& t32)
                      __attribute__((always_inline)) {
     float mx = sj[0];
 #pragma unroll
@@ -314,12 +334,14 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_amdgcn_ldexpf(acc[db][r], k);
+      if constexpr (!PP) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lsum[r] = __builtin_amdgcn_ldexpf(lsum[r], k);
+        for (int r = 0; r < 16; ++r) lsum[r] = __builtin_amdgcn_ldexpf(lsum[r], k);
+      }
       L32 = __builtin_amdgcn_ldexpf(L32, k);
     }
     m2 = m_new;
-    softmax(sj, pj, t32);
+    softmax(sj, pj, pjl, t32);
   };
 
   auto qk_mfma = [&](const lds_char* Kt, f32x16& sj) __attribute__((always_inline)) {
@@ -330,7 +352,8 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
               Kt + (kk / KB) * BLK + kbase[kk % KB]),
           qf[kk], kk == 0 ? zero16 : sj, 0, 0, 0);
   };
-  auto pv_mfma = [&](const lds_char* Vt, const bf16x8 (&pj)[2]) __attribute__((always_inline)) {
+  auto pv_mfma = [&](const lds_char* Vt, const bf16x8 (&pj)[2], const bf16x8 (&pjl)[2])
+                     __attribute__((always_inline)) {
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -342,10 +365,15 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
                                                           pj[half], acc[db], 0, 0, 0);
+        if constexpr (PP)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
+                                                            pjl[half], acc[db], 0, 0, 0);
       }
+    if constexpr (!PP) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-      lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pj[half], lsum, 0, 0, 0);
+      for (int half = 0; half < 2; ++half)
+        lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pj[half], lsum, 0, 0, 0);
+    }
   };
 
   for (int sb = 0; sb < nblk; ++sb) {
@@ -414,7 +442,10 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[1][h][e] = (__bf16)0.0f;
+        for (int e = 0; e < 8; ++e) {
+          pf[1][h][e] = (__bf16)0.0f;
+          if constexpr (PP) pl[1][h][e] = (__bf16)0.0f;
+        }
       wait_copies();
       __syncthreads();
       qk_mfma(Kl, s[0]);
@@ -427,8 +458,8 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         vcopy(t + V_AHEAD, (t + V_AHEAD) % NBUF);
         const lds_char* Vt = Vl + ((t + NBUF - 1) % NBUF) * TB;  // V(t-1)
         const lds_char* Kt = Kl + ((t + 1) % NBUF) * TB;         // K(t+1)
-        constexpr int NPV = 2 * DB;   // PV(t-1) MFMAs
-        constexpr int NV = NPV + 2;   // ... and the row sums of P(t-1)
+        constexpr int NPV = 2 * DB;   // PV(t-1) V fragments (PP: two MFMAs each)
+        constexpr int NV = NPV + (PP ? 0 : 2);  // ... and the row sums of P(t-1)
         constexpr int NM = NV + KK;   // ... and QK^T(t+1)
         auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
           if (i < NPV) {
@@ -450,12 +481,15 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         // elements of tile t; scheduling barriers keep the chunks in order, so
         // the exponentials and sums issue while the matrix core is busy.
         float a4[4], pe[16];
-        uint32_t pw[8];  // P of tile t, bf16 pairs
+        uint32_t pw[8], lw[8];  // P of tile t, bf16 pairs (PP: and residual pairs)
         auto element = [&](int r) __attribute__((always_inline)) {
           pe[r] = __builtin_amdgcn_exp2f(fmaf(s[P][r], c_log2, -m2));
           if (r < 4) a4[r] = pe[r];
           else a4[r & 3] += pe[r];
-          if (r & 1) pw[r >> 1] = cvt_pk_bf16(pe[r - 1], pe[r]);
+          if (r & 1) {
+            pw[r >> 1] = cvt_pk_bf16(pe[r - 1], pe[r]);
+            if constexpr (PP) lw[r >> 1] = residual(pe[r - 1], pe[r], pw[r >> 1]);
+          }
         };
         bf16x8 ob[FWD_PF];
 #pragma unroll
@@ -468,6 +502,9 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
             const int half = i / DB, db = i % DB;
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][half], acc[db], 0, 0,
                                                               0);
+            if constexpr (PP)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pl[P ^ 1][half], acc[db], 0,
+                                                                0, 0);
           } else if (i < NV) {
             lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][i - NPV], lsum, 0, 0, 0);
           } else {
@@ -483,10 +520,10 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         ts32 = (a4[0] + a4[1]) + (a4[2] + a4[3]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const u32x4 q4 = {pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]};
-          pf[P][h] = __builtin_bit_cast(bf16x8, q4);
+          pf[P][h] = pack(pw, h);
+          if constexpr (PP) pl[P][h] = pack(lw, h);
         }
-        if (__ballot(ts32 > TILE_SUM_MAX)) reraise(s[P], pf[P], ts32);
+        if (__ballot(ts32 > TILE_SUM_MAX)) reraise(s[P], pf[P], pl[P], ts32);
         L32 += ts32;
         wait_copies_but<2 * IPW>();
         __syncthreads();
@@ -501,9 +538,9 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       // PV(last); its V tile landed two iterations ago.
       if (t < n_main) {
         iter(t, I0{});
-        pv_mfma(Vl + (last % NBUF) * TB, pf[0]);
+        pv_mfma(Vl + (last % NBUF) * TB, pf[0], pl[0]);
       } else {
-        pv_mfma(Vl + (last % NBUF) * TB, pf[1]);
+        pv_mfma(Vl + (last % NBUF) * TB, pf[1], pl[1]);
       }
       wait_copies();  // redundant re-copies may still be in flight
       __syncthreads();
@@ -544,17 +581,18 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
               if (!vis) s[0][r] = -INFINITY;
             }
           }
-          reraise(s[0], pf[0], ts32);
+          reraise(s[0], pf[0], pl[0], ts32);
           L32 += ts32;
-          pv_mfma(Vt, pf[0]);
+          pv_mfma(Vt, pf[0], pl[0]);
         }
       }
       __syncthreads();  // the next block refills the buffers
     }
   }  // blocks
 
-  const float l16 = lsum[0];
   const float l32 = xhalf_sum(L32);
+  // O's normaliser: the sum of the weights the PV product used.
+  const float l16 = PP ? l32 : lsum[0];
   if (qrow < Lq) {
     const float inv = l16 > 0.f ? 1.f / l16 : 0.f;
     const int64_t orow_i = GL ? zig(first, qrow) : qrow;
@@ -571,7 +609,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   }
 }
 
-template <bool GL, int W>
+template <bool GL, int W, bool PP = false>
 hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int64_t* q_off,
                          const int64_t* k_off, float* O, float* lse, int BH, int64_t Lq,
                          int64_t Lk, int64_t kv_stride, int64_t koff_stride, int nblk, int first,
@@ -580,13 +618,13 @@ hipError_t launch_blocks(const void* Q, const void* K, const void* V, const int6
   const dim3 grid((unsigned)((int64_t)n_qtiles * BH * nranks));
   const float c_log2 = scale * LOG2E;
   if (D == 128) {
-    hipLaunchKernelGGL((attn_fwd_kernel<128, GL, W>), grid, dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_kernel<128, GL, W, PP>), grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
                        BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, nranks,
                        causal ? 1 : 0,
                        c_log2, n_qtiles);
   } else {
-    hipLaunchKernelGGL((attn_fwd_kernel<64, GL, W>), grid, dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_kernel<64, GL, W, PP>), grid, dim3(NTHREADS), 0, stream,
                        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q_off, k_off, O, lse,
                        BH, (int)Lq, (int)Lk, kv_stride, koff_stride, nblk, first, nranks,
                        causal ? 1 : 0,
@@ -614,7 +652,10 @@ hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_al
 
 hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, float* O, float* lse,
                              int BH, int64_t Lr, int N, int rank_lo, int nranks, int D,
-                             bool causal, float scale, hipStream_t stream) {
+                             bool causal, float scale, bool precise, hipStream_t stream) {
+  if (precise)
+    return launch_blocks<true, 8, true>(Q, K, V, nullptr, nullptr, O, lse, BH, Lr, Lr, 0, 0, N,
+                                        rank_lo, nranks, D, causal, scale, stream);
   return launch_blocks<true, 8>(Q, K, V, nullptr, nullptr, O, lse, BH, Lr, Lr, 0, 0, N, rank_lo,
                                 nranks, D, causal, scale, stream);
 }

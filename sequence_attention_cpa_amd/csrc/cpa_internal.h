@@ -35,7 +35,7 @@ hipError_t launch_ring_mfma(const void* Q_i, const void* K_all, const void* V_al
 // Lr/2 % 32 == 0; writes only those ranks' rows.
 hipError_t launch_share_mfma(const void* Q, const void* K, const void* V, float* O, float* lse,
                              int BH, int64_t Lr, int N, int rank_lo, int nranks, int D,
-                             bool causal, float scale, hipStream_t stream);
+                             bool causal, float scale, bool precise, hipStream_t stream);
 
 // Partial attention, one query row per thread, fp32 arithmetic throughout
 // (fp32 inputs, and bf16 inputs with D = 16).

@@ -420,10 +420,12 @@ cpa_status cpa_zigzag_permute_rope(const void* src, void* dst, cpa_dtype dt, int
                   "permute+rope launch");
 }
 
-cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
-                             int32_t H, int64_t L, int32_t D, int32_t N,
-                             int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
-                             float* O, float* lse, void* stream) {
+namespace {
+
+cpa_status share_forward(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
+                         int32_t H, int64_t L, int32_t D, int32_t N, int32_t rank_lo,
+                         int32_t rank_hi, int32_t causal, float scale, float* O, float* lse,
+                         bool precise, void* stream) {
   if (dt != CPA_BF16 && dt != CPA_F32) return fail(CPA_EDTYPE, "unknown dtype %d", (int)dt);
   cpa_status st = check_rank_shape(N, L, B, H, D);
   if (st != CPA_OK) return st;
@@ -447,9 +449,27 @@ cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, cpa_dt
   if (!aligned(lse, 4)) return fail(CPA_EINVAL, "lse must be 4-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)D);
   return from_hip(cpa::launch_share_mfma(Q, K, V, O, lse, B * H, Lr, N, rank_lo,
-                                         rank_hi - rank_lo, D, causal != 0, scale,
+                                         rank_hi - rank_lo, D, causal != 0, scale, precise,
                                          (hipStream_t)stream),
                   "global-layout ring launch");
+}
+
+}  // namespace
+
+cpa_status cpa_share_forward(const void* Q, const void* K, const void* V, cpa_dtype dt, int32_t B,
+                             int32_t H, int64_t L, int32_t D, int32_t N,
+                             int32_t rank_lo, int32_t rank_hi, int32_t causal, float scale,
+                             float* O, float* lse, void* stream) {
+  return share_forward(Q, K, V, dt, B, H, L, D, N, rank_lo, rank_hi, causal, scale, O, lse, false,
+                       stream);
+}
+
+cpa_status cpa_share_forward_precise(const void* Q, const void* K, const void* V, cpa_dtype dt,
+                                     int32_t B, int32_t H, int64_t L, int32_t D, int32_t N,
+                                     int32_t rank_lo, int32_t rank_hi, int32_t causal,
+                                     float scale, float* O, float* lse, void* stream) {
+  return share_forward(Q, K, V, dt, B, H, L, D, N, rank_lo, rank_hi, causal, scale, O, lse, true,
+                       stream);
 }
 
 cpa_status cpa_backward_delta(const float* O, const void* dO, cpa_dtype dt, int64_t rows,

@@ -45,6 +45,8 @@ calls = {
                                                              128, 1, 0.0, P, P, None),
     "share_forward": lambda: lib.cpa_share_forward(P, P, P, BF, 1, 4, 1 << 20, 128, 8, 0, 8, 1,
                                                    0.0, P, P, None),
+    "share_forward_precise": lambda: lib.cpa_share_forward_precise(P, P, P, BF, 1, 4, 1 << 20, 128,
+                                                                   8, 0, 8, 1, 0.0, P, P, None),
     "zigzag_permute": lambda: lib.cpa_zigzag_permute(P, P, 2, 1, 4, 1 << 20, 128, P, 8, 0, 8, 1,
                                                      None),
     "backward_delta": lambda: lib.cpa_backward_delta(P, P, BF, 1 << 22, 128, P, None),

@@ -22,7 +22,7 @@ hipError_t launch_ring_mfma(const void*, const void*, const void*, const int64_t
                             float*, float*, int, int64_t, int, int, int, bool, float,
                             hipStream_t) { return hipSuccess; }
 hipError_t launch_share_mfma(const void*, const void*, const void*, float*, float*, int, int64_t,
-                             int, int, int, int, bool, float, hipStream_t) { return hipSuccess; }
+                             int, int, int, int, bool, float, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_partial_rowwise(const void*, const void*, const void*, bool, const int64_t*,
                                   const int64_t*, float*, float*, int, int64_t, int64_t, int, bool,
                                   float, hipStream_t) { return hipSuccess; }

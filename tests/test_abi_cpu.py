@@ -431,13 +431,13 @@ def test_rank_backward_rejects(lib, kw, status):
     assert cpa.last_error() != ""
 
 
-def _share(lib, **kw):
+def _share(lib, precise=False, **kw):
     a = dict(Q=P, K=P, V=P, dt=_lib.CPA_BF16, B=1, H=2, L=512, D=128, N=4, lo=0, hi=4,
              causal=1, scale=0.0, O=P, lse=P, stream=None)
     a.update(kw)
-    return lib.cpa_share_forward(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["H"], a["L"],
-                                 a["D"], a["N"], a["lo"], a["hi"], a["causal"], a["scale"],
-                                 a["O"], a["lse"], a["stream"])
+    fn = lib.cpa_share_forward_precise if precise else lib.cpa_share_forward
+    return fn(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["H"], a["L"], a["D"], a["N"], a["lo"],
+              a["hi"], a["causal"], a["scale"], a["O"], a["lse"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -454,8 +454,9 @@ def _share(lib, **kw):
     (dict(L=1 << 30, H=64), _lib.CPA_ESHAPE),        # 2^28 rows per rank x 64 heads
     (dict(O=P + 4), _lib.CPA_EINVAL),
 ])
-def test_share_forward_rejects(lib, kw, status):
-    assert _share(lib, **kw) == status
+@pytest.mark.parametrize("precise", [False, True], ids=["bf16_p", "precise_p"])
+def test_share_forward_rejects(lib, kw, status, precise):
+    assert _share(lib, precise, **kw) == status
     assert cpa.last_error() != ""
 
 
@@ -552,7 +553,7 @@ def test_share_calls_take_no_position_table():
     with CPA_OK)."""
     import inspect
     decl = header_text()
-    for name in ("cpa_share_forward", "cpa_share_backward"):
+    for name in ("cpa_share_forward", "cpa_share_forward_precise", "cpa_share_backward"):
         i = decl.index(name + "(")
         params = decl[i:decl.index(")", i)]
         assert "pos" not in params and "int64_t" in params, params

@@ -307,12 +307,16 @@ def share_check(name, rank, n_rows, block):
     Qd, Kd, Vd = Q.to(DEV), K.to(DEV), V.to(DEV)
     results = {}
     pos = None
-    modes = (False, True, "global")
+    modes = (False, True, "global", "precise")
     for fused in modes:
         say(f"{name}: GPU rank {rank} fused={fused}")
         pipe = SharePipeline(w.B, w.H, w.L, w.D, w.N, w.causal, Q.dtype, DEV, rank, rank + 1,
-                             fused=bool(fused), global_layout=fused == "global")
-        Od, lsed = pipe.step(Qd, Kd, Vd)
+                             fused=bool(fused), global_layout=fused in ("global", "precise"))
+        if fused == "precise":
+            Od, lsed = cpa.share_forward(Qd, Kd, Vd, w.N, w.causal, rank_lo=rank,
+                                         rank_hi=rank + 1, precise=True)
+        else:
+            Od, lsed = pipe.step(Qd, Kd, Vd)
         pos = pipe.pos_host.numpy()
         if "g" not in results:
             t = sample_rows(w, rank, pos[rank], n_rows // (w.B * w.H), outl)
@@ -328,9 +332,11 @@ def share_check(name, rank, n_rows, block):
                       lambda b, h: widen(V[b, h]), rows, w.causal, block=block)
     Or = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
     lr = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
-    v_scale = w.outlier_mult if w.outlier_in_v else 1.0
     for fused in modes:
         O, lse = results[fused]
+        # bf16 weights leave an error in O proportional to V's largest rows;
+        # the precise weights do not, so their bounds stay unscaled.
+        v_scale = w.outlier_mult if w.outlier_in_v and fused != "precise" else 1.0
         mx, mean = assert_bf16_close(O, lse, Or, lr, f"{name} fused={fused}", v_scale)
         say(f"{name} fused={fused}: max {mx:.3e} mean {mean:.3e}")
 
@@ -342,8 +348,10 @@ def test_rank_forward_128k_share_sampled(rank):
 
 def test_rank_forward_128k_outliers_in_v_sampled():
     """The 128k share with the outlier token rows scaled in V as well as in Q
-    and K: sampled rows of rank 0, all three forward modes.  V's outlier rows
-    are 8 times larger, and so are the O bounds."""
+    and K: sampled rows of rank 0, every forward mode.  V's outlier rows are 8
+    times larger, and so are the O bounds of the bf16-weight modes; the
+    precise-weight ring (cpa_share_forward_precise) meets the unscaled
+    bounds."""
     share_check("128k_qkv", 0, 512, 32)
 
 
@@ -424,6 +432,27 @@ def test_share_forward_global_layout(case):
     O, lse = pipe.step(Q.to(DEV), K.to(DEV), V.to(DEV))
     torch.cuda.synchronize()
     assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
+
+
+@pytest.mark.parametrize("case", SHARE_CASES, ids=[str(c) for c in SHARE_CASES])
+def test_share_forward_precise(case):
+    """The precise-weight ring equals the oracle for every rank, and its O
+    error stays small when some V rows are 64 times larger than the rest
+    (rows of Q, K and V scaled together, as in the outlier workloads)."""
+    B, H, L, N, D, causal = case
+    Q = rand((B, H, L, D), torch.bfloat16, 63)
+    K = rand((B, H, L, D), torch.bfloat16, 64)
+    V = rand((B, H, L, D), torch.float32, 65)
+    rows = torch.from_numpy(np.random.default_rng(5).choice(L, size=max(1, L // 50),
+                                                             replace=False))
+    V[:, :, rows] *= 64.0
+    V = V.to(torch.bfloat16)
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), causal)
+    O, lse = cpa.share_forward(Q.to(DEV), K.to(DEV), V.to(DEV), N, causal, precise=True)
+    torch.cuda.synchronize()
+    mx, mean = assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr,
+                                 str(case))
+    say(f"precise {case}: max {mx:.3e} mean {mean:.3e}")
 
 
 def test_share_forward_rank_subset_leaves_other_rows():
