@@ -35,9 +35,11 @@
 //  * O is divided by the sum of the bf16-rounded P (the weights the PV
 //    product used), so it stays a convex combination of V rows; lse uses the
 //    fp32 sum of the unrounded P.  The bf16 sum comes from the matrix core:
-//    two more MFMAs per tile multiply a row of ones into the same P operand,
-//    which costs less than unpacking and adding the bf16 pairs on the VALU
-//    (and the dot-product instructions stall the matrix pipe).
+//    two 16x16x32 MFMAs per tile (half the cycles of a 32x32x16 one) take
+//    the same P registers as their B operand and a 0/1 mask as A, whose rows
+//    0 and 1 pick the lanes holding queries 0-15 and 16-31; that costs less
+//    than unpacking and adding the bf16 pairs on the VALU (and the
+//    dot-product instructions stall the matrix pipe).
 //  * K and V tiles live in four LDS buffers each; K(t+3) and V(t+2) are
 //    copied during iteration t straight from global memory into LDS
 //    (global_load_lds_dwordx4), and each iteration waits only for the copies
@@ -272,10 +274,18 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   float m2 = M_INIT;      // exponent reference (log2 units): an integer after the first tile
   float L32 = 0.f;        // this lane's share of the fp32 row sum (gives lse)
   // Row sums of the bf16 P (normalise O), accumulated on the matrix core as
-  // ones x P^T: every element of the 32x32 result holds the lane's query sum.
-  f32x16 lsum = {};
-  const bf16x8 ones8 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  // M x P^T with v_mfma_f32_16x16x32_bf16.  As its B operand, lane l's 8
+  // weights of a key half are column l % 16, key group l / 16; the query of
+  // lane l is l % 32, so column n of groups 0 and 2 is query n, of groups 1
+  // and 3 query n + 16.  Result row 4g + j sits in element j of lanes
+  // [16g, 16g + 16): mask rows 0 and 8 take groups 0 and 2, rows 4 and 12
+  // groups 1 and 3 (lane l supplies row l % 16 of group l / 16), so element
+  // 0 of every lane holds the sum of that lane's own query.
+  f32x4 lsum = {};
+  const int mrow = lane & 15;
+  const __bf16 one = (mrow & 3) == 0 && ((mrow >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.f
+                                                                                : (__bf16)0.f;
+  const bf16x8 ones8 = {one, one, one, one, one, one, one, one};
   float ts32;             // the lane's fp32 tile sum, added once the tile passed its check
   const f32x16 zero16 = {};
 
@@ -334,10 +344,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_amdgcn_ldexpf(acc[db][r], k);
-      if constexpr (!PP) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lsum[r] = __builtin_amdgcn_ldexpf(lsum[r], k);
-      }
+      if constexpr (!PP) lsum[0] = __builtin_amdgcn_ldexpf(lsum[0], k);
       L32 = __builtin_amdgcn_ldexpf(L32, k);
     }
     m2 = m_new;
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     if constexpr (!PP) {
 #pragma unroll
       for (int half = 0; half < 2; ++half)
-        lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pj[half], lsum, 0, 0, 0);
+        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pj[half], lsum, 0, 0, 0);
     }
   };
 
@@ -506,7 +513,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
               acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pl[P ^ 1][half], acc[db], 0,
                                                                 0, 0);
           } else if (i < NV) {
-            lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][i - NPV], lsum, 0, 0, 0);
+            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pf[P ^ 1][i - NPV], lsum, 0, 0, 0);
           } else {
             const int kk = i - NV;
             s[P ^ 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[kk],

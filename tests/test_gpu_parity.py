@@ -339,6 +339,16 @@ def share_check(name, rank, n_rows, block):
         v_scale = w.outlier_mult if w.outlier_in_v and fused != "precise" else 1.0
         mx, mean = assert_bf16_close(O, lse, Or, lr, f"{name} fused={fused}", v_scale)
         say(f"{name} fused={fused}: max {mx:.3e} mean {mean:.3e}")
+        if fused == "precise":
+            assert mx <= PRECISE_MAX_ABS and mean <= PRECISE_MEAN_ABS, (mx, mean)
+
+
+# The precise-weight ring carries each weight to a relative 2^-16 (bf16 hi/lo
+# pair), so its O error is that of the fp32 accumulation, far below the bf16
+# bounds; its own bounds sit about 3x above the largest errors it showed
+# (3.4e-4 max with V rows scaled by 64, 3.0e-4 on the V-outlier share).
+PRECISE_MAX_ABS = 1e-3
+PRECISE_MEAN_ABS = 1e-4
 
 
 @pytest.mark.parametrize("rank", [0, 3])
@@ -453,6 +463,7 @@ def test_share_forward_precise(case):
     mx, mean = assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr,
                                  str(case))
     say(f"precise {case}: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= PRECISE_MAX_ABS and mean <= PRECISE_MEAN_ABS, (mx, mean)
 
 
 def test_share_forward_rank_subset_leaves_other_rows():
