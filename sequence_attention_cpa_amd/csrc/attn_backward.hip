@@ -21,14 +21,14 @@
 //    dQ^T += K^T dS^T with K^T read from LDS by ds_read_b64_tr_b16.  The lse
 //    is known, so there is no running max and no rescaling.  The pass walks
 //    the N blocks of a ring in one launch (same order as the forward).
-//  * dK/dV pass: roles swapped.  A workgroup owns 128 keys; Q and dO tiles of
-//    32 queries stream through LDS, with their lse and delta.  Per tile:
-//    S = Q K^T and dP = dO V^T (each lane holds 16 queries of ONE key), P and
-//    dS, then dV^T += dO^T P and dK^T += Q^T dS with the transposed operands
-//    read by ds_read_b64_tr_b16.  Both accumulators and both resident K/V
-//    rows would need about 260 registers per lane, so two waves share each
-//    32-key group and split its products (P role: S, P and dV; dS role: dP,
-//    dS and dK), which keeps two waves per SIMD.
+//  * dK/dV pass: roles swapped.  A workgroup owns 128 keys (32 per wave);
+//    Q and dO tiles of 32 queries stream through LDS, with their lse and
+//    delta.  Per tile each wave computes S = Q K^T and dP = dO V^T (a lane
+//    holds 16 queries of ONE key), P and dS, then dV^T += dO^T P and
+//    dK^T += Q^T dS with the transposed operands read by ds_read_b64_tr_b16.
+//    The exponentials issue between the dP products and dS between the dV
+//    products.  K rows stay in registers and V rows in LDS, so both
+//    accumulators fit at two waves per SIMD; two workgroups share a CU.
 // Causal visibility compares global positions (key position <= query
 // position); positions increase inside every block, so a query's visible keys
 // are a prefix of a block and a key's visible queries a suffix; only tiles
@@ -122,6 +122,104 @@ struct TileAddr {
         (__attribute__((address_space(3))) i16x4*)(b + toff[db][0]));
     const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)(b + toff[db][1]));
+    const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8, v8);
+  }
+};
+
+// The dK/dV pass's tiles use column blocks of W 16-byte chunks instead:
+// logical chunk c of row r sits in 16-byte slot
+// 32W*(c/W) + W*r + ((c%W) ^ cb_key<W>(r)), so a row-operand read is one of
+// W/2 per-lane bases plus a compile-time offset and a transposed read one of
+// two (TileAddr needs KK + 2 DB offset registers).  The XOR key spreads each
+// 16-lane phase of a row read and each 32-lane half of a transposed read
+// over distinct banks.  Copy instruction n fills slots [64n, 64n + 64):
+// 16 rows x 64 bytes (W = 4) or 8 rows x 128 bytes (W = 8, whole lines).
+template <int W>
+__device__ __forceinline__ int cb_key(int r) {
+  if constexpr (W == 4) return (r >> 2) & 3;
+  else return (((r >> 1) & 1) ? 5 : 0) ^ (((r >> 2) & 1) ? 2 : 0) ^ (((r >> 3) & 1) ? 4 : 0);
+}
+template <int W>
+__device__ __forceinline__ int cb_slot(int r, int c) {
+  return 32 * W * (c / W) + W * r + ((c % W) ^ cb_key<W>(r));
+}
+
+template <int D, int W, int NW>
+struct CBTile {
+  using G = Geo<D>;
+  static constexpr int NCP = G::TILE_BYTES / 1024;           // 1 KB copy instructions per tile
+  static constexpr int IPW = NCP >= NW ? NCP / NW : 1;       // per wave
+  static constexpr int KB = W / 2;                           // row-operand bases
+  static constexpr int BLK = 512 * W;                        // bytes per column block
+  static_assert(NCP % NW == 0 || NW > NCP, "copy split");
+  int wv, lane;
+  int rbase[KB];
+  int tbase[2];
+
+  // Copy instruction n: the lane's tile row and its byte offset in global
+  // memory (recomputed per copy: a few VALU instructions instead of
+  // registers held across the loop).
+  __device__ __forceinline__ int crow(int n) const { return (64 / W) * (n % (W / 2)) + lane / W; }
+  __device__ __forceinline__ int coff(int n) const {
+    const int r = crow(n);
+    const int c = W * (n / (W / 2)) + ((lane % W) ^ cb_key<W>(r));
+    return r * G::ROW_BYTES + c * 16;
+  }
+
+  __device__ __forceinline__ CBTile(int wv_, int lane_) : wv(wv_), lane(lane_) {
+    const int hi = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int e = 0; e < KB; ++e) rbase[e] = cb_slot<W>(l32, e * 2 + hi) * 16;
+    const int trow = hi * 4 + ((lane & 15) >> 2);
+    const int tch = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+    const int tsub = (lane & 1) * 8;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      tbase[e] = (W == 4 ? cb_slot<W>(trow + 8 * e, tch) : cb_slot<W>(trow, 4 * e + tch)) * 16 +
+                 tsub;
+  }
+
+  // Rows [row0, row0 + 32) of a [nrows, D] matrix into the tile at LDS byte
+  // address `dst` (wave-uniform, kept in scalar registers); rows past the end
+  // re-read the last row (callers mask them).
+  __device__ __forceinline__ void copy(const __bf16* src, int64_t row0, int64_t nrows,
+                                       uint32_t dst) const {
+    const __bf16* base = src + row0 * D;
+    if (row0 + BN <= nrows) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int n = (wv * IPW + i) % NCP;
+        copy16_saddr((uint32_t)coff(n), base, dst + (uint32_t)n * 1024u);
+      }
+    } else {
+      const int last = (int)(nrows - 1 - row0);  // last valid tile row (< 31)
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int n = (wv * IPW + i) % NCP;
+        const int over = crow(n) - last;
+        copy16_saddr((uint32_t)(coff(n) - (over > 0 ? over : 0) * G::ROW_BYTES), base,
+                     dst + (uint32_t)n * 1024u);
+      }
+    }
+  }
+
+  // Row operand: lane's tile row l32, logical chunk kk*2 + hi.
+  __device__ __forceinline__ bf16x8 rows(const lds_char* t, int kk) const {
+    return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+        t + (kk / KB) * BLK + rbase[kk % KB]);
+  }
+
+  // Transposed operand: column d of block db, rows h*16 + trow + 8p (p = 0, 1).
+  __device__ __forceinline__ int taddr(int h, int db, int p) const {
+    if constexpr (W == 4) return h * 1024 + db * 2048 + tbase[p];
+    else return h * 2048 + (db >> 1) * 4096 + p * 1024 + tbase[p ^ (db & 1)];
+  }
+  __device__ __forceinline__ bf16x8 trans(const lds_char* t, int h, int db) const {
+    const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(t + taddr(h, db, 0)));
+    const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(t + taddr(h, db, 1)));
     const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     return __builtin_bit_cast(bf16x8, v8);
   }
@@ -371,19 +469,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
 
 // ------------------------------------------------------------- dK/dV pass
 
-// Eight waves per workgroup, two per SIMD, for 128 keys: waves w and w + 4
-// share key group w (32 keys) and split every tile's four products evenly.
-// Wave w (P role) forms S = Q K^T and P, hands P to its partner through LDS,
-// and accumulates dV^T += dO^T P; wave w + 4 (dS role) forms dP = dO V^T,
-// then dS = P (dP - delta) from the partner's P, and accumulates
-// dK^T += Q^T dS.  A barrier in the middle of each tile publishes P.  Each
-// wave keeps one 32 x D accumulator and one of K / V, so two waves fit per
-// SIMD, and no product is computed twice.
+// Four waves per workgroup, 32 keys each (128 keys), two workgroups per CU,
+// so the two waves on a SIMD belong to independent workgroups and one's
+// softmax arithmetic runs beside the other's matrix products.  Each wave does
+// all four products of its keys against every query tile: S = Q K^T and
+// dP = dO V^T (each lane then holds 16 queries of ONE key), P and dS on the
+// VALU, then dV^T += dO^T P and dK^T += Q^T dS.  The wave's K rows stay in
+// registers (B operand of S); its V rows are staged in LDS once (B operand
+// of dP), which keeps both 32 x D accumulators in registers at two waves per
+// SIMD.  Q and dO tiles stream through LDS (double buffered) with their lse
+// and delta; one barrier per tile.
 // GL: all tensors in global token order ([BH, nblk * Lq, ...]); the queries
 // are rank `qrank`'s rows and K/V block b (with its dK/dV rows) is rank b's,
 // all through zig_row.
 template <int D, bool GL>
-__global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ dK,
@@ -395,17 +495,18 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   constexpr int DB = G::DB;
   __shared__ __attribute__((aligned(1024))) char q_lds_raw[2 * TB];
   __shared__ __attribute__((aligned(1024))) char o_lds_raw[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char v_lds_raw[4 * TB];  // V rows, one tile per wave
   __shared__ __attribute__((aligned(16))) float l2_lds[2][BN];
   __shared__ __attribute__((aligned(16))) float dl_lds[2][BN];
-  __shared__ __attribute__((aligned(16))) float4 p_lds[4][4][64];  // [key group][r/4][lane]
   lds_char* const Ql = (lds_char*)q_lds_raw;
   lds_char* const Ol = (lds_char*)o_lds_raw;
+  // the same tiles as scalar LDS byte addresses for the copies
+  const uint32_t Ql_s = __builtin_amdgcn_readfirstlane(lds_addr(Ql));
+  const uint32_t Ol_s = __builtin_amdgcn_readfirstlane(lds_addr(Ol));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0 .. 7
-  const int kg = wv & 3;                                     // key group
-  const bool dk_role = wv >= 4;                              // dS role
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0 .. 3: key group
   const int hi = lane >> 5;
   const int l32 = lane & 31;
   const int bh = blockIdx.x % BH;
@@ -414,9 +515,12 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
   const int blk = rest / n_ktiles;
   const int64_t k_base = (int64_t)kt * BM;
   const int64_t last_key = (k_base + BM < Lk ? k_base + BM : Lk) - 1;
-  const int64_t krow = k_base + kg * 32 + l32;
+  const int64_t kw0 = k_base + wv * 32;  // first key of this wave
+  const int64_t krow = kw0 + l32;
   const int64_t krow_c = krow < Lk ? krow : Lk - 1;
   const float c_log2 = scale * LOG2E;
+  lds_char* const Vw = (lds_char*)v_lds_raw + wv * TB;
+  const uint32_t Vw_s = __builtin_amdgcn_readfirstlane(lds_addr(Vw));
 
   const int64_t Lrow = GL ? Lq * nblk : Lq;  // rows per head of every tensor (GL)
   // Row of key u of this block within a head.
@@ -460,154 +564,216 @@ __global__ __launch_bounds__(2 * NTHREADS, 1) void bwd_dkdv_kernel(
     }
   }
   if (m_lo >= Lq) return;  // no query sees any key of this workgroup: nothing to add
+  const int my_first32 = (int)my_first;  // <= Lq <= 2^30
   const int t0 = (int)(m_lo / BN);
   const int T = (int)((Lq + BN - 1) / BN);
 
-  const TileAddr<D, 8> ta(wv, lane);
+  constexpr int W = 4;
+  const CBTile<D, W, 4> ta(wv, lane);
   // Query tile t (rows [t*BN, t*BN + BN)) of Q or dO into LDS.
-  auto copy_q = [&](const __bf16* lo, const __bf16* hi_base, int t, lds_char* dst)
+  auto copy_q = [&](const __bf16* lo, const __bf16* hi_base, int t, uint32_t dst)
                     __attribute__((always_inline)) {
     const int64_t u0 = (int64_t)t * BN;
     ta.copy((GL && u0 >= Cq) ? hi_base : lo, u0, Lq, dst);
   };
   const f32x16 zero16 = {};
 
-  // lse reference and delta of query tile t into LDS buffer b (first wave).
-  // A tile's rows are contiguous in either layout (GL: inside one chunk), so
+  // lse and delta of query tile t (first wave): loaded when the tile's
+  // copies are issued, written to LDS buffer b (as the exp2 reference) at the
+  // end of the iteration, so the loads have the whole tile to land.  A
+  // tile's rows are contiguous in either layout (GL: inside one chunk), so
   // the row address is the chunk base plus the local row.
-  auto stage_rows = [&](int t, int b) __attribute__((always_inline)) {
+  float row_l = 0.f, row_d = 0.f;
+  auto load_rows = [&](int t) __attribute__((always_inline)) {
     if (tid < BN) {
       const int64_t q = (int64_t)t * BN + tid;
       const int64_t base = (GL && (int64_t)t * BN >= Cq) ? q_hi_row : q_lo_row;
-      l2_lds[b][tid] = q < Lq ? lse_ref(lse_bh[base + q]) : INFINITY;
-      dl_lds[b][tid] = q < Lq ? dl_bh[base + q] : 0.f;
+      const int64_t qc = q < Lq ? q : Lq - 1;
+      row_l = lse_bh[base + qc];
+      row_d = dl_bh[base + qc];
+    }
+  };
+  auto store_rows = [&](int t, int b) __attribute__((always_inline)) {
+    if (tid < BN) {
+      const bool ok = (int64_t)t * BN + tid < Lq;
+      l2_lds[b][tid] = ok ? lse_ref(row_l) : INFINITY;
+      dl_lds[b][tid] = ok ? row_d : 0.f;
     }
   };
 
-  // The whole pass for one role; both roles run the same copies, staging
-  // and barriers, so the workgroup stays in step.
-  auto run = [&](auto DKR_) __attribute__((always_inline)) {
-    constexpr bool DKR = decltype(DKR_)::value;
-    // This lane's key row of K (P role) or V (dS role) as the B operand.
-    bf16x8 rf[KK];
-    {
-      const __bf16* src = (DKR ? Vb : Kb) + kmap(krow_c) * D;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        rf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16 + hi * 8);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) settle(rf[kk]);
+  // The wave's 32 V rows into its LDS tile (GL: 32 keys from a multiple of 32
+  // lie in one chunk, so they are contiguous); rows past Lk re-read the last.
+  {
+    const CBTile<D, W, 1> tv(0, lane);
+    if constexpr (GL) {
+      const int64_t n = Lk - kw0;
+      tv.copy(Vb + kmap(kw0 < Lk ? kw0 : Lk - 1) * D, 0, n < BN ? (n > 0 ? n : 1) : BN, Vw_s);
+    } else {
+      tv.copy(Vb, kw0 < Lk ? kw0 : Lk - 1, Lk, Vw_s);
     }
-    f32x16 acc[DB];  // dV^T (P role) or dK^T (dS role), D x 32 keys
+  }
+  // This lane's key row of K as the B operand of S = Q K^T.
+  bf16x8 kf[KK];
+  {
+    const __bf16* src = Kb + kmap(krow_c) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      kf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16 + hi * 8);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) settle(kf[kk]);
+  }
+  f32x16 dv[DB], dk[DB];  // dV^T and dK^T, D x 32 keys
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dv[db][r] = 0.f;
+      dk[db][r] = 0.f;
+    }
+
+  auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
+    constexpr int P = decltype(P_)::value;
+    if (t + 1 < T) {
+      copy_q(Qbh, Qbh_hi, t + 1, Ql_s + (P ^ 1) * TB);
+      copy_q(Obh, Obh_hi, t + 1, Ol_s + (P ^ 1) * TB);
+      load_rows(t + 1);
+    }
+    const lds_char* Qt = Ql + P * TB;
+    const lds_char* Ot = Ol + P * TB;
+    const int64_t q0 = (int64_t)t * BN;
+    // 32 products per tile, each emitted as one chunk with its slice of the
+    // VALU work so that the exponentials and dS issue while the matrix core
+    // runs (scheduling barriers keep the chunks in order):
+    //   chunks  0- 7  S = Q K^T (kk)
+    //   chunks  8-15  dP = dO V^T (kk), exp of two S rows each
+    //   chunks 16-23  dV^T += dO^T P (half, column block), dS of two rows each
+    //   chunks 24-31  dK^T += Q^T dS (half, column block)
+    // A operands (and dP's V rows) are read PF chunks ahead.
+    constexpr int NM = 4 * KK, PF = 2;
+    constexpr int RPC = 16 / KK;  // score rows per chunk of the exp and dS slices
+    static_assert(KK == 2 * DB && RPC * KK == 16, "chunk table");
+    using RowV = std::conditional_t<RPC == 2, float2, float4>;
+    f32x16 s = zero16, dp = zero16;
+    u32x4 pf[2], sf[2];  // P and dS as bf16 pairs (B operands, key halves of the queries)
+    // A chunk's operands: A (and dP's V rows as B), and the lse references
+    // (dP chunks) or deltas (dV chunks) of the score rows it works on; rows
+    // r .. r + RPC - 1 (r a multiple of RPC) are queries acc_row(r, hi) + 0 ..
+    // RPC - 1.  They are read in one go, PF chunks ahead; reading the row
+    // values right after the operands keeps LDS returns (in order) from
+    // making a chunk wait for a later chunk's reads.
+    struct Ops {
+      bf16x8 a, b;
+      RowV rv;
+    };
+    auto rows_of = [&](const float(&arr)[BN], int r) __attribute__((always_inline)) -> RowV {
+      return *reinterpret_cast<const RowV*>(&arr[acc_row(r, hi)]);
+    };
+    auto fetch = [&](int i) __attribute__((always_inline)) -> Ops {
+      Ops o;
+      if (i < KK) {
+        o.a = ta.rows(Qt, i);
+      } else if (i < 2 * KK) {
+        o.a = ta.rows(Ot, i - KK);
+        o.b = ta.rows(Vw, i - KK);
+        o.rv = rows_of(l2_lds[P], (i - KK) * RPC);
+      } else {
+        const int j = (i - 2 * KK) % (2 * DB);
+        o.a = ta.trans(i < 3 * KK ? Ot : Qt, j / DB, j % DB);
+        if (i < 3 * KK) o.rv = rows_of(dl_lds[P], (i - 2 * KK) * RPC);
+      }
+      return o;
+    };
+    auto rvel = [](const RowV& v, int e) __attribute__((always_inline)) -> float {
+      if constexpr (RPC == 2) return e == 0 ? v.x : v.y;
+      else return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    };
+    Ops ob[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ob[i] = fetch(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i == KK) {
+        __builtin_amdgcn_sched_barrier(0);
+        // hidden queries (tiles crossing a key's causal bound) get P = 0:
+        // tile row u is hidden when u < my_first - q0
+        if (q0 < m_hi) {
+          const int lim64 = my_first32 - (int)q0;
+          const int lim = lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (acc_row(r, hi) < lim) s[r] = -INFINITY;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const Ops cur = ob[i % PF];
+      if (i + PF < NM) ob[i % PF] = fetch(i + PF);
+      if (i < KK) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a, kf[i], i == 0 ? zero16 : s, 0, 0, 0);
+      } else if (i < 2 * KK) {
+        const int c = i - KK;
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a, cur.b, c == 0 ? zero16 : dp, 0, 0, 0);
+        // P of rows [c RPC, (c + 1) RPC), in place of S
+#pragma unroll
+        for (int e = 0; e < RPC; e += 2) {
+          const int r = c * RPC + e;
+          s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -rvel(cur.rv, e)));
+          s[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c_log2, -rvel(cur.rv, e + 1)));
+          pf[r >> 3][(r >> 1) & 3] = cvt_pk_bf16(s[r], s[r + 1]);
+        }
+      } else if (i < 3 * KK) {
+        const int j = i - 2 * KK, h = j / DB, db = j % DB;
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a, __builtin_bit_cast(bf16x8, pf[h]),
+                                                         dv[db], 0, 0, 0);
+        // dS of rows [j RPC, (j + 1) RPC)
+#pragma unroll
+        for (int e = 0; e < RPC; e += 2) {
+          const int r = j * RPC + e;
+          dp[r] = s[r] * (dp[r] - rvel(cur.rv, e));
+          dp[r + 1] = s[r + 1] * (dp[r + 1] - rvel(cur.rv, e + 1));
+          sf[r >> 3][(r >> 1) & 3] = cvt_pk_bf16(dp[r], dp[r + 1]);
+        }
+      } else {
+        const int j = i - 3 * KK, h = j / DB, db = j % DB;
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a, __builtin_bit_cast(bf16x8, sf[h]),
+                                                         dk[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_copies();
+    if (t + 1 < T) store_rows(t + 1, P ^ 1);
+    __syncthreads();
+  };
+
+  copy_q(Qbh, Qbh_hi, t0, Ql_s);
+  copy_q(Obh, Obh_hi, t0, Ol_s);
+  load_rows(t0);
+  wait_copies();
+  store_rows(t0, 0);
+  __syncthreads();
+  int t = t0;
+  for (; t + 1 < T; t += 2) {
+    iter(t, I0{});
+    iter(t + 1, I1{});
+  }
+  if (t < T) iter(t, I0{});
+
+  if (krow < Lk) {
+    const int64_t row = GL ? ((int64_t)bh * Lrow + kmap(krow)) * D
+                           : blk * kv_stride + ((int64_t)bh * Lk + krow) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float4* const pslot = &p_lds[kg][0][lane];
-
-    auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
-      constexpr int P = decltype(P_)::value;
-      if (t + 1 < T) {
-        copy_q(Qbh, Qbh_hi, t + 1, Ql + (P ^ 1) * TB);
-        copy_q(Obh, Obh_hi, t + 1, Ol + (P ^ 1) * TB);
+      for (int gq = 0; gq < 4; ++gq) {
+        const int c = db * 32 + gq * 8 + hi * 4;
+        float4* pk = reinterpret_cast<float4*>(dK + row + c);
+        float4* pv = reinterpret_cast<float4*>(dV + row + c);
+        const float4 ok = *pk, ov = *pv;
+        *pk = float4{ok.x + dk[db][gq * 4 + 0] * scale, ok.y + dk[db][gq * 4 + 1] * scale,
+                     ok.z + dk[db][gq * 4 + 2] * scale, ok.w + dk[db][gq * 4 + 3] * scale};
+        *pv = float4{ov.x + dv[db][gq * 4 + 0], ov.y + dv[db][gq * 4 + 1],
+                     ov.z + dv[db][gq * 4 + 2], ov.w + dv[db][gq * 4 + 3]};
       }
-      const lds_char* Qt = Ql + P * TB;
-      const lds_char* Ot = Ol + P * TB;
-      const int64_t q0 = (int64_t)t * BN;
-      // S = Q K^T (P role) or dP = dO V^T (dS role): lane holds its key's
-      // 16 queries, rows acc_row(r, hi) = g*8 + hi*4 + (r & 3), r = 4g .. 4g+3.
-      // Then P (published through LDS) or dS, then dV^T += dO^T P or
-      // dK^T += Q^T dS.
-      f32x16 x = zero16;
-      bf16x8 wf[2];
-      mfma_phases<KK, 2 * DB, 3>(
-          [&](int i) __attribute__((always_inline)) -> bf16x8 {
-            if (i < KK) return ta.rows(DKR ? Ot : Qt, i);
-            const int j = i - KK;
-            return ta.trans(DKR ? Qt : Ot, j / DB, j % DB);
-          },
-          [&](int i, const bf16x8& op) __attribute__((always_inline)) {
-            if (i < KK) {
-              x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, rf[i], x, 0, 0, 0);
-            } else {
-              const int j = i - KK;
-              acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, wf[j / DB], acc[j % DB],
-                                                                    0, 0, 0);
-            }
-          },
-          [&]() __attribute__((always_inline)) {
-            if constexpr (!DKR) {
-              if (q0 < m_hi) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                  if (q0 + acc_row(r, hi) < my_first) x[r] = -INFINITY;
-              }
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const float4 a = *reinterpret_cast<const float4*>(&l2_lds[P][g * 8 + hi * 4]);
-                const float l2[4] = {a.x, a.y, a.z, a.w};
-                float pv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  pv[e] = __builtin_amdgcn_exp2f(fmaf(x[g * 4 + e], c_log2, -l2[e]));
-                  wf[(g * 4 + e) >> 3][(g * 4 + e) & 7] = (__bf16)pv[e];
-                }
-                pslot[g * 64] = float4{pv[0], pv[1], pv[2], pv[3]};
-              }
-            }
-            __syncthreads();  // P of this tile is in LDS
-            if constexpr (DKR) {
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const float4 pv = pslot[g * 64];
-                const float4 b = *reinterpret_cast<const float4*>(&dl_lds[P][g * 8 + hi * 4]);
-                const float p4[4] = {pv.x, pv.y, pv.z, pv.w};
-                const float d4[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int r = g * 4 + e;
-                  wf[r >> 3][r & 7] = (__bf16)(p4[e] * (x[r] - d4[e]));
-                }
-              }
-            }
-          });
-      if (t + 1 < T) stage_rows(t + 1, P ^ 1);
-      wait_copies();
-      __syncthreads();
-    };
-
-    copy_q(Qbh, Qbh_hi, t0, Ql);
-    copy_q(Obh, Obh_hi, t0, Ol);
-    stage_rows(t0, 0);
-    wait_copies();
-    __syncthreads();
-    int t = t0;
-    for (; t + 1 < T; t += 2) {
-      iter(t, I0{});
-      iter(t + 1, I1{});
-    }
-    if (t < T) iter(t, I0{});
-
-    if (krow < Lk) {
-      float* dst = (DKR ? dK : dV) +
-                   (GL ? ((int64_t)bh * Lrow + kmap(krow)) * D
-                       : blk * kv_stride + ((int64_t)bh * Lk + krow) * D);
-      const float f = DKR ? scale : 1.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          float4* p = reinterpret_cast<float4*>(dst + db * 32 + gq * 8 + hi * 4);
-          const float4 o = *p;
-          *p = float4{o.x + acc[db][gq * 4 + 0] * f, o.y + acc[db][gq * 4 + 1] * f,
-                      o.z + acc[db][gq * 4 + 2] * f, o.w + acc[db][gq * 4 + 3] * f};
-        }
-    }
-  };
-  if (dk_role)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+  }
 }
 
 // ------------------------------------------------------------- delta
@@ -836,7 +1002,7 @@ hipError_t mfma_bwd(const void* Q, const void* K, const void* V, const void* dO,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, GL>), dim3((unsigned)(nblk * n_ktiles * BH)),
-                     dim3(2 * NTHREADS), 0, st, (const __bf16*)Q, (const __bf16*)K,
+                     dim3(NTHREADS), 0, st, (const __bf16*)Q, (const __bf16*)K,
                      (const __bf16*)V, (const __bf16*)dO, lse, delta, q_off, k_off, dK, dV, BH,
                      Lq, Lk, kv_stride, koff_stride, causal ? 1 : 0, scale, n_ktiles, nblk,
                      first);
