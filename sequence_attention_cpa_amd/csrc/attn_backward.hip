@@ -18,9 +18,11 @@
 //    double buffered), Q and dO rows stay in registers.  Per tile:
 //    S^T = K Q^T and dP^T = V dO^T (each lane then holds 16 keys of ONE query,
 //    so lse and delta are one register each), P and dS on the VALU, then
-//    dQ^T += K^T dS^T with K^T read from LDS by ds_read_b64_tr_b16.  The lse
-//    is known, so there is no running max and no rescaling.  The pass walks
-//    the N blocks of a ring in one launch (same order as the forward).
+//    dQ^T += K^T dS^T with K^T read from LDS by ds_read_b64_tr_b16; the
+//    exponentials issue between the dP products and half of dS between the
+//    dQ products.  The lse is known, so there is no running max and no
+//    rescaling.  The pass walks the N blocks of a ring in one launch (same
+//    order as the forward).
 //  * dK/dV pass: roles swapped.  A workgroup owns 128 keys (32 per wave);
 //    Q and dO tiles of 32 queries stream through LDS, with their lse and
 //    delta.  Per tile each wave computes S = Q K^T and dP = dO V^T (a lane
@@ -366,39 +368,66 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     const lds_char* Kt = Kl + P * TB;
     const lds_char* Vt = Vl + P * TB;
     f32x16 s = zero16, dp = zero16;
-    bf16x8 dsf[2];
+    u32x4 dsf[2];  // dS^T as bf16 pairs (B operand, key halves)
     const int64_t u0 = (int64_t)t * BN;
-    // S^T, dP^T (K and V rows alternate), then dS, then dQ^T += K^T dS^T.
-    mfma_phases<2 * KK, 2 * DB, 3>(
-        [&](int i) __attribute__((always_inline)) -> bf16x8 {
-          if (i < 2 * KK) return ta.rows((i & 1) ? Vt : Kt, i >> 1);
-          const int j = i - 2 * KK;
-          return ta.trans(Kt, j / DB, j % DB);
-        },
-        [&](int i, const bf16x8& op) __attribute__((always_inline)) {
-          if (i < 2 * KK) {
-            if (i & 1)
-              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, df[i >> 1], dp, 0, 0, 0);
-            else
-              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[i >> 1], s, 0, 0, 0);
-          } else {
-            const int j = i - 2 * KK;
-            acc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, dsf[j / DB], acc[j % DB], 0,
-                                                                  0, 0);
-          }
-        },
-        [&]() __attribute__((always_inline)) {
-          if (u0 + BN > n_lo) {
+    // Chunks, each one product with its slice of the VALU work (scheduling
+    // barriers keep them in order, so the VALU issues while the matrix core
+    // runs):
+    //   0 .. KK-1        S^T = K Q^T
+    //   KK .. 2KK-1      dP^T = V dO^T, the exponentials of 16/KK S rows each
+    //   2KK .. 3KK-1     dQ^T += K^T dS^T (half, column block); dS of the
+    //                    first key half before it, of the second during it
+    constexpr int NM = 3 * KK, PF = 3, RPC = 16 / KK;
+    static_assert(KK == 2 * DB && RPC * KK == 16, "chunk table");
+    auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      if (i < KK) return ta.rows(Kt, i);
+      if (i < 2 * KK) return ta.rows(Vt, i - KK);
+      const int j = i - 2 * KK;
+      return ta.trans(Kt, j / DB, j % DB);
+    };
+    auto ds_rows = [&](int r0, int r1) __attribute__((always_inline)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (u0 + acc_row(r, hi) >= my_n) s[r] = -INFINITY;
-          }
+      for (int r = r0; r < r1; r += 2) {
+        const float d0 = s[r] * (dp[r] - dl), d1 = s[r + 1] * (dp[r + 1] - dl);
+        dsf[r >> 3][(r >> 1) & 3] = cvt_pk_bf16(d0, d1);
+      }
+    };
+    bf16x8 ob[PF];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l2));
-            dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
-          }
-        });
+    for (int i = 0; i < PF; ++i) ob[i] = fetch(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i == KK) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (u0 + BN > n_lo) {  // keys past a row's causal bound: P = 0
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (u0 + acc_row(r, hi) >= my_n) s[r] = -INFINITY;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == 2 * KK) {
+        ds_rows(0, 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bf16x8 cur = ob[i % PF];
+      if (i + PF < NM) ob[i % PF] = fetch(i + PF);
+      if (i < KK) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], i == 0 ? zero16 : s, 0, 0, 0);
+      } else if (i < 2 * KK) {
+        const int c = i - KK;
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, df[c], c == 0 ? zero16 : dp, 0, 0, 0);
+#pragma unroll
+        for (int r = c * RPC; r < (c + 1) * RPC; ++r)
+          s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l2));
+      } else {
+        const int j = i - 2 * KK, h = j / DB, db = j % DB;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, dsf[h]),
+                                                          acc[db], 0, 0, 0);
+        if (h == 0) ds_rows(8 + db * (8 / DB), 8 + (db + 1) * (8 / DB));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_copies();
     __syncthreads();
   };
