@@ -44,13 +44,14 @@
 //    copied during iteration t straight from global memory into LDS
 //    (global_load_lds_dwordx4), and each iteration waits only for the copies
 //    of the iteration before, so a copy has two iterations to land.
-//  * Tiles are classified per wave from the block's key positions: tiles
-//    every row of the wave fully sees (the steady loop, which every wave of
-//    the workgroup runs up to the first wave's count), and the few that cross
-//    a row's causal bound or the block end (a simple, non-pipelined tail with
-//    an element mask and an exact row max).  Keys visible to a causal row are
-//    a prefix of the block (positions increase).  Rows that see no key write
-//    O = 0, lse = -inf.
+//  * Tiles are classified from the block's key positions: tiles every row of
+//    the workgroup fully sees (the steady loop), and the few that cross a
+//    row's causal bound or the block end.  In the global layout every tile is
+//    whole and the steady loop runs the crossing tiles too, masking each
+//    element by the lane's count of visible keys; the rank-major build runs
+//    them in a simple, non-pipelined tail with an element mask and an exact
+//    row max.  Keys visible to a causal row are a prefix of the block
+//    (positions increase).  Rows that see no key write O = 0, lse = -inf.
 //  * Global layout (cpa_share_forward): Q, K, V, O, lse are the whole sequence
 //    in token order and rank r's local row u is global row zig(r, u) (chunk r
 //    for u < C, chunk 2N-1-r after, C = L/(2N)); the positions are that same
@@ -425,10 +426,20 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     }
     if (w0 >= Lq) w_full = w_tot = 0;  // a wave past the last row stores nothing
     if (n_tot == 0) continue;          // no row of the workgroup sees this block
+    // GL: every tile is whole (Lk is a multiple of 32), so the steady loop
+    // also runs the tiles that cross a row's causal bound, masking each
+    // element by the lane's count of visible keys in this block (keys are
+    // sorted by position); waves whose rows see none of such a tile compute
+    // it with every weight 0.  The rank-major path keeps them for the tail.
+    const int n_loop = GL ? n_tot : n_main;
+    int my_cnt = 0;
+    if constexpr (GL) {
+      if (causal) my_cnt = (int)zig_count_le(blk, nblk, C, my_qpos);
+    }
 
-    // ---- steady loop over tiles [0, n_main): every wave sees all of them ----
-    if (n_main > 0) {
-      const int last = n_main - 1;
+    // ---- steady loop over tiles [0, n_loop): every wave sees [0, n_main) ----
+    if (n_loop > 0) {
+      const int last = n_loop - 1;
       auto kcopy = [&](int j, int buf) __attribute__((always_inline)) {
         const int jj = j < last ? j : last;
         copy_full(tile_src(Kbh, Kbh_hi, jj), Kl + buf * TB);
@@ -459,8 +470,15 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
 
       // Iteration t: copies of K(t+3), V(t+2); PV(t-1) and QK^T(t+1) on the
       // matrix cores next to the softmax of tile t; the overflow check.
-      auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
+      auto iter = [&](int t, auto P_, auto M_) __attribute__((always_inline)) {
         constexpr int P = decltype(P_)::value;
+        constexpr bool MASK = decltype(M_)::value;
+        // masked tiles: tile row u of this lane's row is visible when u < lim
+        int lim = 0;
+        if constexpr (MASK) {
+          const int l = my_cnt - t * 32;
+          lim = l < 0 ? 0 : (l > 32 ? 32 : l);
+        }
         kcopy(t + K_AHEAD, (t + K_AHEAD) % NBUF);
         vcopy(t + V_AHEAD, (t + V_AHEAD) % NBUF);
         const lds_char* Vt = Vl + ((t + NBUF - 1) % NBUF) * TB;  // V(t-1)
@@ -490,6 +508,9 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         float a4[4], pe[16];
         uint32_t pw[8], lw[8];  // P of tile t, bf16 pairs (PP: and residual pairs)
         auto element = [&](int r) __attribute__((always_inline)) {
+          if constexpr (MASK) {
+            if ((r >> 2) * 8 + hi * 4 + (r & 3) >= lim) s[P][r] = -INFINITY;
+          }
           pe[r] = __builtin_amdgcn_exp2f(fmaf(s[P][r], c_log2, -m2));
           if (r < 4) a4[r] = pe[r];
           else a4[r & 3] += pe[r];
@@ -537,31 +558,43 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       };
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
+      using NOM = std::false_type;
+      // Pairs keep the tile parity static; masked pairs start at an even
+      // tile (masking a tile every row fully sees changes nothing).
+      const int n_plain = GL ? (n_main & ~1) : n_main;
       int t = 0;
-      for (; t + 1 < n_main; t += 2) {
-        iter(t, I0{});
-        iter(t + 1, I1{});
+      for (; t + 1 < n_plain; t += 2) {
+        iter(t, I0{}, NOM{});
+        iter(t + 1, I1{}, NOM{});
+      }
+      if constexpr (GL) {
+        using MSK = std::true_type;
+        for (; t + 1 < n_loop; t += 2) {
+          iter(t, I0{}, MSK{});
+          iter(t + 1, I1{}, MSK{});
+        }
+        if (t < n_loop) iter(t, I0{}, MSK{});
+      } else {
+        if (t < n_loop) iter(t, I0{}, NOM{});
       }
       // PV(last); its V tile landed two iterations ago.
-      if (t < n_main) {
-        iter(t, I0{});
-        pv_mfma(Vl + (last % NBUF) * TB, pf[0], pl[0]);
-      } else {
+      if (last & 1)
         pv_mfma(Vl + (last % NBUF) * TB, pf[1], pl[1]);
-      }
+      else
+        pv_mfma(Vl + (last % NBUF) * TB, pf[0], pl[0]);
       wait_copies();  // redundant re-copies may still be in flight
       __syncthreads();
     }
 
-    // ---- tail: tiles [n_main, n_tot), per wave full, masked or skipped ----
-    if (n_tot > n_main) {
+    // ---- tail: tiles [n_loop, n_tot), per wave full, masked or skipped ----
+    if (n_tot > n_loop) {
       auto tcopy = [&](int j) __attribute__((always_inline)) {
         const int buf = j % NBUF;
         copy_any(tile_src(Kbh, Kbh_hi, j), j, Kl + buf * TB);
         copy_any(tile_src(Vbh, Vbh_hi, j), j, Vl + buf * TB);
       };
-      tcopy(n_main);
-      for (int t = n_main; t < n_tot; ++t) {
+      tcopy(n_loop);
+      for (int t = n_loop; t < n_tot; ++t) {
         if (t + 1 < n_tot) {
           tcopy(t + 1);
           wait_copies_but<2 * IPW>();
