@@ -19,9 +19,9 @@ LSE_REL = 1e-3
 F32_RTOL, F32_ATOL = 1e-5, 1e-6
 
 
-# Backward, bf16 inputs: P and dS are rounded to bf16 (relative 2^-9) before
+# Backward, bf16 inputs: P and dS are rounded to bf16 (relative 2^-8) before
 # the matrix products, whose sums are fp32, so every gradient entry carries an
-# error of a small multiple of 2^-9 times the size of its terms.  Checked
+# error of a small multiple of 2^-8 times the size of its terms.  Checked
 # against the largest entry of the reference gradient (entries near zero
 # carry the same absolute error as large ones), norm-wise, and on the mean:
 # max |d| <= 7e-3 max|ref|, ||d||_2 <= 5e-3 ||ref||_2, mean |d| <= 5e-3
