@@ -184,10 +184,11 @@ struct CBTile {
 
   // Rows [row0, row0 + 32) of a [nrows, D] matrix into the tile at LDS byte
   // address `dst` (wave-uniform, kept in scalar registers); rows past the end
-  // re-read the last row (callers mask them).
-  __device__ __forceinline__ void copy(const __bf16* src, int64_t row0, int64_t nrows,
+  // re-read the last row (callers mask them).  Row counts are 32-bit (at most
+  // 2^30 rows), so the bound checks stay on the scalar unit.
+  __device__ __forceinline__ void copy(const __bf16* src, int row0, int nrows,
                                        uint32_t dst) const {
-    const __bf16* base = src + row0 * D;
+    const __bf16* base = src + (int64_t)row0 * D;
     if (row0 + BN <= nrows) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
@@ -195,7 +196,7 @@ struct CBTile {
         copy16_saddr((uint32_t)coff(n), base, dst + (uint32_t)n * 1024u);
       }
     } else {
-      const int last = (int)(nrows - 1 - row0);  // last valid tile row (< 31)
+      const int last = nrows - 1 - row0;  // last valid tile row (< 31)
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int n = (wv * IPW + i) % NCP;
@@ -600,10 +601,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
   constexpr int W = 4;
   const CBTile<D, W, 4> ta(wv, lane);
   // Query tile t (rows [t*BN, t*BN + BN)) of Q or dO into LDS.
+  const int Cq32 = (int)Cq;
+  const int Lq32 = (int)Lq;
   auto copy_q = [&](const __bf16* lo, const __bf16* hi_base, int t, uint32_t dst)
                     __attribute__((always_inline)) {
-    const int64_t u0 = (int64_t)t * BN;
-    ta.copy((GL && u0 >= Cq) ? hi_base : lo, u0, Lq, dst);
+    const int u0 = t * BN;
+    ta.copy((GL && u0 >= Cq32) ? hi_base : lo, u0, (int)Lq, dst);
   };
   const f32x16 zero16 = {};
 
@@ -612,19 +615,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
   // end of the iteration, so the loads have the whole tile to land.  A
   // tile's rows are contiguous in either layout (GL: inside one chunk), so
   // the row address is the chunk base plus the local row.
+  // (32-bit row indices: Lq <= 2^30; the per-lane part is one register.)
   float row_l = 0.f, row_d = 0.f;
   auto load_rows = [&](int t) __attribute__((always_inline)) {
     if (tid < BN) {
-      const int64_t q = (int64_t)t * BN + tid;
-      const int64_t base = (GL && (int64_t)t * BN >= Cq) ? q_hi_row : q_lo_row;
-      const int64_t qc = q < Lq ? q : Lq - 1;
-      row_l = lse_bh[base + qc];
-      row_d = dl_bh[base + qc];
+      const int64_t base = (GL && t * BN >= Cq32) ? q_hi_row : q_lo_row;
+      const int q = t * BN + tid;
+      const int qc = q < Lq32 ? q : Lq32 - 1;
+      row_l = (lse_bh + base)[qc];
+      row_d = (dl_bh + base)[qc];
     }
   };
   auto store_rows = [&](int t, int b) __attribute__((always_inline)) {
     if (tid < BN) {
-      const bool ok = (int64_t)t * BN + tid < Lq;
+      const bool ok = t * BN + tid < Lq32;
       l2_lds[b][tid] = ok ? lse_ref(row_l) : INFINITY;
       dl_lds[b][tid] = ok ? row_d : 0.f;
     }
@@ -636,9 +640,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     const CBTile<D, W, 1> tv(0, lane);
     if constexpr (GL) {
       const int64_t n = Lk - kw0;
-      tv.copy(Vb + kmap(kw0 < Lk ? kw0 : Lk - 1) * D, 0, n < BN ? (n > 0 ? n : 1) : BN, Vw_s);
+      tv.copy(Vb + kmap(kw0 < Lk ? kw0 : Lk - 1) * D, 0, n < BN ? (n > 0 ? (int)n : 1) : BN, Vw_s);
     } else {
-      tv.copy(Vb, kw0 < Lk ? kw0 : Lk - 1, Lk, Vw_s);
+      tv.copy(Vb, (int)(kw0 < Lk ? kw0 : Lk - 1), (int)Lk, Vw_s);
     }
   }
   // This lane's key row of K as the B operand of S = Q K^T.
@@ -678,7 +682,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     //   chunks 16-23  dV^T += dO^T P (half, column block), dS of two rows each
     //   chunks 24-31  dK^T += Q^T dS (half, column block)
     // A operands (and dP's V rows) are read PF chunks ahead.
-    constexpr int NM = 4 * KK, PF = 2;
+    constexpr int NM = 4 * KK, PF = 1;
     constexpr int RPC = 16 / KK;  // score rows per chunk of the exp and dS slices
     static_assert(KK == 2 * DB && RPC * KK == 16, "chunk table");
     using RowV = std::conditional_t<RPC == 2, float2, float4>;
@@ -689,7 +693,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     // r .. r + RPC - 1 (r a multiple of RPC) are queries acc_row(r, hi) + 0 ..
     // RPC - 1.  They are read in one go, PF chunks ahead; reading the row
     // values right after the operands keeps LDS returns (in order) from
-    // making a chunk wait for a later chunk's reads.
+    // making a chunk wait for a later chunk's reads.  One chunk ahead: a
+    // deeper ring costs the registers that keep spill reloads (whose waits
+    // also wait for the tile copies in flight) out of the loop.
     struct Ops {
       bf16x8 a, b;
       RowV rv;
