@@ -54,8 +54,8 @@ constexpr int64_t kMaxBH = 65535;
 // A dispatch counts its work-items along x in 32 bits.  The matrix-core
 // kernels (bf16, D = 64 or 128) launch cpa::kMfmaThreads threads on every
 // cpa::kMfmaRows query rows of every (b, h) pair; the backward's dK/dV pass
-// launches twice that on every kMfmaRows key rows of every (b, h) pair and
-// K/V block.  nblk_bwd = 0 checks the forward launch only.
+// launches as many on every kMfmaRows key rows of every (b, h) pair and K/V
+// block.  nblk_bwd = 0 checks the forward launch only.
 cpa_status check_mfma_launch(cpa_dtype dt, int32_t D, int64_t BH, int64_t Lq, int64_t Lk,
                              int64_t nblk_bwd) {
   if (dt != CPA_BF16 || (D != 64 && D != 128)) return CPA_OK;
@@ -65,7 +65,7 @@ cpa_status check_mfma_launch(cpa_dtype dt, int32_t D, int64_t BH, int64_t Lq, in
   if (qt > lim / (BH * cpa::kMfmaThreads))
     return fail(CPA_ESHAPE, "launch of %lld query rows x %lld heads exceeds 2^32 work-items",
                 (long long)Lq, (long long)BH);
-  if (nblk_bwd > 0 && kt > lim / (BH * 2 * cpa::kMfmaThreads) / nblk_bwd)
+  if (nblk_bwd > 0 && kt > lim / (BH * cpa::kMfmaThreads) / nblk_bwd)
     return fail(CPA_ESHAPE, "backward launch of %lld blocks x %lld key rows x %lld heads exceeds "
                             "2^32 work-items",
                 (long long)nblk_bwd, (long long)Lk, (long long)BH);
