@@ -484,7 +484,7 @@ def _share_bwd(lib, **kw):
     (dict(O=None), _lib.CPA_EINVAL),
     (dict(dK=P + 4), _lib.CPA_EINVAL),
     (dict(lse=P + 2), _lib.CPA_EINVAL),
-    (dict(N=1 << 22, L=1 << 28), _lib.CPA_ESHAPE),   # 2^22 blocks x 2 heads x 512 threads
+    (dict(N=1 << 23, L=1 << 29), _lib.CPA_ESHAPE),   # 2^23 blocks x 2 heads x 256 threads
 ])
 def test_share_backward_rejects(lib, kw, status):
     assert _share_bwd(lib, **kw) == status
