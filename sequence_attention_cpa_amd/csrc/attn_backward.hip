@@ -56,85 +56,14 @@ constexpr float LOG2E = 1.4426950408889634f;
 using I0 = std::integral_constant<int, 0>;
 using I1 = std::integral_constant<int, 1>;
 
-// Per-lane addressing of a 32-row tile of D bf16 columns in LDS, swizzled by
-// swz<D>: the async copy of a tile, the row-major operand (lane = row l32,
-// 8 columns starting at kk*16 + hi*8) and the transposed operand (lane = column
-// d of block db, 8 consecutive rows of half `h`, as two 4-row reads).
-template <int D, int NW>
-struct TileAddr {
-  using G = Geo<D>;
-  static constexpr int NCOPY = G::TILE_BYTES / 1024;         // 1 KB copy instructions per tile
-  static constexpr int IPW = NCOPY >= NW ? NCOPY / NW : 1;  // per copying wave
-  static constexpr int CW = NCOPY / IPW;                    // waves that copy
-  int coff[IPW];
-  int crow[IPW];
-  int roff[G::KK];
-  int toff[G::DB][2];
-  int wv;
-
-  __device__ __forceinline__ TileAddr(int wv_, int lane) : wv(wv_) {
-    const int hi = lane >> 5, l32 = lane & 31;
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int n = (wv % CW) * IPW + i;
-      crow[i] = n * G::RPI + lane / G::CHUNKS;
-      coff[i] = crow[i] * G::ROW_BYTES + swz<D>(crow[i], lane % G::CHUNKS) * 16;
-    }
-#pragma unroll
-    for (int kk = 0; kk < G::KK; ++kk)
-      roff[kk] = l32 * G::ROW_BYTES + swz<D>(l32, kk * 2 + hi) * 16;
-    const int trow = hi * 4 + ((lane & 15) >> 2);
-    const int tch = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
-    const int tsub = (lane & 1) * 8;
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        toff[db][p] = (trow + 8 * p) * G::ROW_BYTES + swz<D>(trow + 8 * p, db * 4 + tch) * 16 + tsub;
-  }
-
-  // Rows [row0, row0 + 32) of a [nrows, D] matrix into `dst`; rows past the
-  // end re-read the last row (callers mask them).
-  __device__ __forceinline__ void copy(const __bf16* src, int64_t row0, int64_t nrows,
-                                       lds_char* dst) const {
-    if (wv >= CW) return;  // uniform per wave
-    if (row0 + BN <= nrows) {
-      const __bf16* base = src + row0 * D;
-#pragma unroll
-      for (int i = 0; i < IPW; ++i)
-        copy16_saddr((uint32_t)coff[i], base, lds_addr(dst + (wv * IPW + i) * 1024));
-    } else {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        int64_t u = row0 + crow[i];
-        u = u < nrows ? u : nrows - 1;
-        const char* g = (const char*)(src + u * D) + (coff[i] - crow[i] * G::ROW_BYTES);
-        copy16_vaddr(g, lds_addr(dst + (wv * IPW + i) * 1024));
-      }
-    }
-  }
-
-  __device__ __forceinline__ bf16x8 rows(const lds_char* t, int kk) const {
-    return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(t + roff[kk]);
-  }
-
-  __device__ __forceinline__ bf16x8 trans(const lds_char* t, int h, int db) const {
-    const lds_char* b = t + h * 16 * G::ROW_BYTES;
-    const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(b + toff[db][0]));
-    const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(b + toff[db][1]));
-    const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    return __builtin_bit_cast(bf16x8, v8);
-  }
-};
-
-// The dK/dV pass's tiles use column blocks of W 16-byte chunks instead:
-// logical chunk c of row r sits in 16-byte slot
-// 32W*(c/W) + W*r + ((c%W) ^ cb_key<W>(r)), so a row-operand read is one of
-// W/2 per-lane bases plus a compile-time offset and a transposed read one of
-// two (TileAddr needs KK + 2 DB offset registers).  The XOR key spreads each
-// 16-lane phase of a row read and each 32-lane half of a transposed read
+// Per-lane addressing of a 32-row tile of D bf16 columns in LDS, in column
+// blocks of W 16-byte chunks: logical chunk c of row r sits in 16-byte slot
+// 32W*(c/W) + W*r + ((c%W) ^ cb_key<W>(r)).  A row-operand read (lane = row
+// l32, 8 columns from kk*16 + hi*8) is then one of W/2 per-lane bases plus a
+// compile-time offset, and a transposed read (lane = column d of block db,
+// 8 consecutive rows of half h, as two 4-row reads) one of two; a per-element
+// XOR swizzle would need KK + 2 DB offset registers.  The XOR key spreads
+// each 16-lane phase of a row read and each 32-lane half of a transposed read
 // over distinct banks.  Copy instruction n fills slots [64n, 64n + 64):
 // 16 rows x 64 bytes (W = 4) or 8 rows x 128 bytes (W = 8, whole lines).
 template <int W>
@@ -292,6 +221,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char v_lds_raw[2 * TB];
   lds_char* const Kl = (lds_char*)k_lds_raw;
   lds_char* const Vl = (lds_char*)v_lds_raw;
+  // the same tiles as scalar LDS byte addresses for the copies
+  const uint32_t Kl_s = __builtin_amdgcn_readfirstlane(lds_addr(Kl));
+  const uint32_t Vl_s = __builtin_amdgcn_readfirstlane(lds_addr(Vl));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -337,7 +269,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
       settle(df[kk]);
     }
   }
-  const TileAddr<D, 4> ta(wv, lane);
+  const CBTile<D, 4, 4> ta(wv, lane);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -354,17 +286,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   int64_t n_lo = Lk, n_hi = Lk, my_n = Lk;
   int T = 0;
   // Tile t (keys [t*BN, t*BN + BN)) of the current block's K or V into LDS.
-  auto copy_kv = [&](const __bf16* lo, const __bf16* hi_base, int t, lds_char* dst)
+  auto copy_kv = [&](const __bf16* lo, const __bf16* hi_base, int t, uint32_t dst)
                      __attribute__((always_inline)) {
-    const int64_t u0 = (int64_t)t * BN;
-    ta.copy((GL && u0 >= C) ? hi_base : lo, u0, Lk, dst);
+    const int u0 = t * BN;  // 32-bit row counts: at most 2^30 rows
+    ta.copy((GL && u0 >= (int)C) ? hi_base : lo, u0, (int)Lk, dst);
   };
 
   auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
     constexpr int P = decltype(P_)::value;
     if (t + 1 < T) {
-      copy_kv(Kbh, Kbh_hi, t + 1, Kl + (P ^ 1) * TB);
-      copy_kv(Vbh, Vbh_hi, t + 1, Vl + (P ^ 1) * TB);
+      copy_kv(Kbh, Kbh_hi, t + 1, Kl_s + (P ^ 1) * TB);
+      copy_kv(Vbh, Vbh_hi, t + 1, Vl_s + (P ^ 1) * TB);
     }
     const lds_char* Kt = Kl + P * TB;
     const lds_char* Vt = Vl + P * TB;
@@ -467,8 +399,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     }
     if (n_hi == 0) continue;
     T = (int)((n_hi + BN - 1) / BN);
-    copy_kv(Kbh, Kbh_hi, 0, Kl);
-    copy_kv(Vbh, Vbh_hi, 0, Vl);
+    copy_kv(Kbh, Kbh_hi, 0, Kl_s);
+    copy_kv(Vbh, Vbh_hi, 0, Vl_s);
     wait_copies();
     __syncthreads();
     int t = 0;

@@ -24,26 +24,12 @@ constexpr int BN = 32;         // rows of one LDS tile (keys, or queries in the 
 
 template <int D>
 struct Geo {
-  static constexpr int CHUNKS = D / 8;               // 16-byte chunks per row
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one K or V tile
   static constexpr int KK = D / 16;                  // MFMA k-steps over d
   static constexpr int DB = D / 32;                  // 32-wide d blocks of O^T
-  static constexpr int RPI = 1024 / ROW_BYTES;       // tile rows per 1 KB copy instruction
-  static constexpr int IPW = TILE_BYTES / 1024 / 4;  // copy instructions per wave per tile
-  static_assert(IPW >= 1, "tile smaller than one copy instruction per wave");
+  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB copy instructions");
 };
-
-// Physical 16-byte chunk holding logical chunk c of tile row r (an XOR, so
-// it is its own inverse).  Depends on r only through r % 16.
-template <int D>
-__device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (D == 128) {
-    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
-  } else {
-    return c ^ ((r >> 1) & 7);
-  }
-}
 
 // Zigzag layout, closed form: rank r of nblk holds chunk r, then chunk
 // 2nblk-1-r, C rows each.  Its local row u is global row (and position)
