@@ -55,9 +55,12 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(ring):
+def pmc_traffic(ring, workload):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    counter runs, or None when they were taken on a different version of it."""
+    counter runs, or None when they were taken on a different version of it
+    or on another workload (the runs profile the 128k share)."""
+    if workload != "128k":
+        return None
     try:
         with open(PMC_FILES[ring]) as f:
             d = json.load(f)
@@ -490,7 +493,7 @@ def main():
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": pmc_traffic(args.ring), "kernel": dom_kernel,
+                     "traffic": pmc_traffic(args.ring, args.workload), "kernel": dom_kernel,
                      "launch_ms": round(dom_ms, 4), "launch_ms_from": dom_src,
                      "useful_flop_per_launch": dom_flop},
         "kernels": {

@@ -44,3 +44,20 @@ def test_causal_pairs_of_a_contiguous_split():
     for r in range(N):
         got = sum(bench.causal_pairs(pos[r], pos[j]) for j in range(N))
         assert got == r * Lr * Lr + Lr * (Lr + 1) // 2
+
+
+def test_traffic_comes_from_the_committed_counters_of_the_same_kernel_and_workload():
+    """The roofline's traffic figure is the profiled 128k launch's, taken on
+    the attention source as it stands; other workloads report none."""
+    import json
+    with open(bench.PMC_FILES["global"]) as f:
+        d = json.load(f)
+    got = bench.pmc_traffic("global", "128k")
+    if d.get("kernel_sha") == bench.kernel_sha():
+        assert got == d["traffic_bytes_per_launch"] > 0
+        assert d["traffic_bytes_per_launch"] == (d["read_bytes_per_launch"]
+                                                 + d["write_bytes_per_launch"])
+    else:
+        assert got is None
+    for other in ("12k", "1m", "128k_qkv"):
+        assert bench.pmc_traffic("global", other) is None
