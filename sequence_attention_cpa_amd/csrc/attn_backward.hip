@@ -617,15 +617,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     constexpr int NM = 4 * KK, PF = 1;
     constexpr int RPC = 16 / KK;  // score rows per chunk of the exp and dS slices
     static_assert(KK == 2 * DB && RPC * KK == 16, "chunk table");
-    using RowV = std::conditional_t<RPC == 2, float2, float4>;
+    using RowV = float4;  // the lse / delta values of a group of 4 rows
     f32x16 s = zero16, dp = zero16;
     u32x4 pf[2], sf[2];  // P and dS as bf16 pairs (B operands, key halves of the queries)
-    // A chunk's operands: A (and dP's V rows as B), and the lse references
-    // (dP chunks) or deltas (dV chunks) of the score rows it works on; rows
-    // r .. r + RPC - 1 (r a multiple of RPC) are queries acc_row(r, hi) + 0 ..
-    // RPC - 1.  They are read in one go, PF chunks ahead; reading the row
-    // values right after the operands keeps LDS returns (in order) from
-    // making a chunk wait for a later chunk's reads.  One chunk ahead: a
+    // A chunk's operands: A (and dP's V rows as B), and, for the first chunk
+    // of each group of 4 score rows, the group's lse references (dP chunks)
+    // or deltas (dV chunks): rows 4g .. 4g + 3 are queries acc_row(4g, hi) +
+    // 0 .. 3, one 16-byte read.  They are read in one go, PF chunks ahead;
+    // reading the row values right after the operands keeps LDS returns (in
+    // order) from making a chunk wait for a later chunk's reads.  One chunk ahead: a
     // deeper ring costs the registers that keep spill reloads (whose waits
     // also wait for the tile copies in flight) out of the loop.
     struct Ops {
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
       RowV rv;
     };
     auto rows_of = [&](const float(&arr)[BN], int r) __attribute__((always_inline)) -> RowV {
-      return *reinterpret_cast<const RowV*>(&arr[acc_row(r, hi)]);
+      return *reinterpret_cast<const RowV*>(&arr[acc_row(r & ~3, hi)]);
     };
     auto fetch = [&](int i) __attribute__((always_inline)) -> Ops {
       Ops o;
@@ -642,18 +642,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
       } else if (i < 2 * KK) {
         o.a = ta.rows(Ot, i - KK);
         o.b = ta.rows(Vw, i - KK);
-        o.rv = rows_of(l2_lds[P], (i - KK) * RPC);
+        if (((i - KK) * RPC) % 4 == 0) o.rv = rows_of(l2_lds[P], (i - KK) * RPC);
       } else {
         const int j = (i - 2 * KK) % (2 * DB);
         o.a = ta.trans(i < 3 * KK ? Ot : Qt, j / DB, j % DB);
-        if (i < 3 * KK) o.rv = rows_of(dl_lds[P], (i - 2 * KK) * RPC);
+        if (i < 3 * KK && ((i - 2 * KK) * RPC) % 4 == 0)
+          o.rv = rows_of(dl_lds[P], (i - 2 * KK) * RPC);
       }
       return o;
     };
     auto rvel = [](const RowV& v, int e) __attribute__((always_inline)) -> float {
-      if constexpr (RPC == 2) return e == 0 ? v.x : v.y;
-      else return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+      return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
     };
+    RowV rg;  // the current group's values
     Ops ob[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) ob[i] = fetch(i);
@@ -674,6 +675,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
       }
       const Ops cur = ob[i % PF];
       if (i + PF < NM) ob[i % PF] = fetch(i + PF);
+      if (i >= KK && i < 3 * KK && ((i - KK) % KK * RPC) % 4 == 0) rg = cur.rv;
       if (i < KK) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a, kf[i], i == 0 ? zero16 : s, 0, 0, 0);
       } else if (i < 2 * KK) {
@@ -683,8 +685,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < RPC; e += 2) {
           const int r = c * RPC + e;
-          s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -rvel(cur.rv, e)));
-          s[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c_log2, -rvel(cur.rv, e + 1)));
+          s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -rvel(rg, r & 3)));
+          s[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c_log2, -rvel(rg, (r + 1) & 3)));
           pf[r >> 3][(r >> 1) & 3] = cvt_pk_bf16(s[r], s[r + 1]);
         }
       } else if (i < 3 * KK) {
@@ -695,8 +697,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < RPC; e += 2) {
           const int r = j * RPC + e;
-          dp[r] = s[r] * (dp[r] - rvel(cur.rv, e));
-          dp[r + 1] = s[r + 1] * (dp[r + 1] - rvel(cur.rv, e + 1));
+          dp[r] = s[r] * (dp[r] - rvel(rg, r & 3));
+          dp[r + 1] = s[r + 1] * (dp[r + 1] - rvel(rg, (r + 1) & 3));
           sf[r >> 3][(r >> 1) & 3] = cvt_pk_bf16(dp[r], dp[r + 1]);
         }
       } else {
