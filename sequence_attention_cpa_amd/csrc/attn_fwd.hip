@@ -27,23 +27,35 @@
 //    end of the block, to a slow path that is taken a few times per row.
 //  * No per-tile row max.  The exponent reference m is an integer (log2
 //    units) fixed by the first tile a row sees; every later tile computes
-//    P = 2^(s*c - m) directly and checks its fp32 sum.  A sum above 2^40
-//    means some score outgrew the reference by more than 2^36: the slow path
-//    then takes the tile's real max, raises m to its ceiling, rescales O and
-//    the sums by the exact power of two and redoes the tile.  P stays below
-//    2^40, so bf16 P and the fp32 accumulators cannot overflow.
+//    P = 2^(s*c - m) directly and checks the largest of its weights (eight
+//    v_max3 per lane).  A weight above 2^40 means a score outgrew the
+//    reference by more than 40: the slow path then takes the tile's real
+//    score max, raises m to its ceiling, rescales O and the sums by the
+//    exact power of two and redoes the tile.  P stays at most 2^40, so bf16
+//    P and the fp32 accumulators cannot overflow.
 //  * O is divided by the sum of the bf16-rounded P (the weights the PV
-//    product used), so it stays a convex combination of V rows; lse uses the
-//    fp32 sum of the unrounded P.  The bf16 sum comes from the matrix core:
-//    two 16x16x32 MFMAs per tile (half the cycles of a 32x32x16 one) take
-//    the same P registers as their B operand and a 0/1 mask as A, whose rows
-//    0 and 1 pick the lanes holding queries 0-15 and 16-31; that costs less
+//    product used), so it stays a convex combination of V rows.  That sum
+//    comes from the matrix core: two 16x16x32 MFMAs per tile (half the
+//    cycles of a 32x32x16 one) take the same P registers as their B operand
+//    and a 0/1 mask as A (layout at the accumulator below); that costs less
 //    than unpacking and adding the bf16 pairs on the VALU (and the
-//    dot-product instructions stall the matrix pipe).
-//  * K and V tiles live in four LDS buffers each; K(t+3) and V(t+2) are
-//    copied during iteration t straight from global memory into LDS
-//    (global_load_lds_dwordx4), and each iteration waits only for the copies
-//    of the iteration before, so a copy has two iterations to land.
+//    dot-product instructions stall the matrix pipe).  lse is the log of
+//    that sum plus what rounding took off the largest weight each lane saw
+//    (p - bf16(p)): a row that one key dominates would otherwise carry that
+//    key's rounding, up to 2^-9 relative, into lse.  The largest weight
+//    comes free with the overflow check (its max chain starts from the
+//    running max).  An fp32 sum of all weights (16 adds per lane and tile)
+//    measured 2 % slower at the 128k share and 3 % at 12k.
+//  * K and V tiles live in eight LDS buffers each (128 KiB at D = 128);
+//    K(t+5) and V(t+4) are copied during iteration t straight from global
+//    memory into LDS (global_load_lds_dwordx4).  The workgroup meets at a
+//    barrier after every second iteration only: each pair of iterations
+//    waits for the copies of the pair before and publishes them to the pair
+//    after, so a copy has two to four iterations to land and the waves
+//    drift freely within a pair.  The first two V fragments of the next
+//    iteration's PV are read before the pair's barrier (that tile was
+//    published one pair earlier), so the matrix core does not wait for LDS
+//    after it.
 //  * Tiles are classified from the block's key positions: tiles every row of
 //    the workgroup fully sees (the steady loop), and the few that cross a
 //    row's causal bound or the block end.  In the global layout every tile is
@@ -62,7 +74,8 @@
 //    hi = bf16(P) and lo = bf16(P - hi), and the PV product runs twice per V
 //    fragment, once on each part.  hi + lo carries P to a relative 2^-16, so
 //    the bf16 rounding of P no longer limits O, and O is divided by the fp32
-//    sum instead (no matrix-core row sums).  It costs 8 MFMAs per tile
+//    sum instead (no matrix-core row sums); lse and the overflow check use
+//    that fp32 sum too (a sum above 2^40 takes the slow path).  It costs 8 MFMAs per tile
 //    (24 instead of 18 at D = 128) and about 40 VALU instructions.
 #include "cpa_internal.h"
 #include "mfma_tile.h"
@@ -83,17 +96,25 @@ constexpr int BM = 32 * WAVES;       // query rows per workgroup
 constexpr int NTHREADS = 64 * WAVES;
 static_assert(NTHREADS * cpa::kMfmaRows == BM * cpa::kMfmaThreads,
               "the host checks launch sizes with two threads per query row");
-constexpr int NBUF = 4;     // LDS buffers per operand
-constexpr int K_AHEAD = 3;  // iteration t copies K(t + K_AHEAD); at most NBUF
-constexpr int V_AHEAD = 2;  // iteration t copies V(t + V_AHEAD); at most NBUF - 2
-static_assert(K_AHEAD <= NBUF && V_AHEAD <= NBUF - 2, "copy would overwrite a tile in use");
+// LDS buffers per operand, and how far ahead iteration t copies: K(t +
+// K_AHEAD), V(t + V_AHEAD).  With a barrier after every odd iteration, the
+// pair of iterations (2q, 2q+1) reads K(2q+1..2q+2) and V(2q-1..2q+1) (the
+// last one for the next pair's first PV), the copies of the pair before
+// are landing and the pair's own copies go to K(2q+5..2q+6) and
+// V(2q+4..2q+5): K_AHEAD = 5 and V_AHEAD = 4 are the distances at which a
+// pair's copies are read two pairs later, and 6 K and 7 V tiles are in use
+// at once.
+constexpr int NBUF = 8;
+constexpr int K_AHEAD = 5;
+constexpr int V_AHEAD = 4;
+static_assert(K_AHEAD + 1 <= NBUF && V_AHEAD + 3 <= NBUF, "copy would overwrite a tile in use");
 // Operand reads in flight ahead of the MFMA that uses them (2 to 6 measured
-// within 1.5 %).
-constexpr int FWD_PF = 3;
+// within 1.5 %; 2 is the fastest with the carried reads below).
+constexpr int FWD_PF = 2;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-// A lane's 16 weights of a tile summing above this send the wave to the slow
-// path (some weight exceeds 2^36).
+// A lane's largest weight of a tile above this (precise weights: its 16
+// weights summing above it) sends the wave to the slow path.
 constexpr float TILE_SUM_MAX = 0x1p40f;
 // Reference before a row's first tile: any finite score overflows against it.
 constexpr float M_INIT = -0x1p100f;
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   bf16x8 pf[2][2];        // bf16 P of two tiles, by tile parity, key halves
   bf16x8 pl[2][2];        // PP: the residuals P - hi, same indexing
   float m2 = M_INIT;      // exponent reference (log2 units): an integer after the first tile
-  float L32 = 0.f;        // this lane's share of the fp32 row sum (gives lse)
+  float L32 = 0.f;        // PP: the lane's share of the fp32 row sum; else its largest weight
   // Row sums of the bf16 P (normalise O), accumulated on the matrix core as
   // M x P^T with v_mfma_f32_16x16x32_bf16.  As its B operand, lane l's 8
   // weights of a key half are column l % 16, key group l / 16; the query of
@@ -287,7 +308,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   const __bf16 one = (mrow & 3) == 0 && ((mrow >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.f
                                                                                 : (__bf16)0.f;
   const bf16x8 ones8 = {one, one, one, one, one, one, one, one};
-  float ts32;             // the lane's fp32 tile sum, added once the tile passed its check
+  float ts32;             // the lane's largest weight of the tile (PP: fp32 tile sum)
   const f32x16 zero16 = {};
 
   // bf16 residuals of a packed pair: bf16(p0 - hi0), bf16(p1 - hi1), where
@@ -303,7 +324,8 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     return __builtin_bit_cast(bf16x8, q4);
   };
   // Weights of one tile at the current reference: P packed to bf16 for the
-  // PV product (PP: and its residuals) and the lane's fp32 sum.
+  // PV product (PP: and its residuals) and the lane's largest weight (PP:
+  // the lane's fp32 sum).
   auto softmax = [&](const f32x16& sj, bf16x8 (&pj)[2], bf16x8 (&pjl)[2], float& t32)
                      __attribute__((always_inline)) {
     float a[4];
@@ -312,17 +334,21 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     for (int r = 0; r < 16; r += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sj[r], c_log2, -m2));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sj[r + 1], c_log2, -m2));
-      if (r < 4) {
-        a[r] = p0;
-        a[r + 1] = p1;
+      if constexpr (PP) {
+        if (r < 4) {
+          a[r] = p0;
+          a[r + 1] = p1;
+        } else {
+          a[r & 3] += p0;
+          a[(r + 1) & 3] += p1;
+        }
       } else {
-        a[r & 3] += p0;
-        a[(r + 1) & 3] += p1;
+        a[0] = r == 0 ? fmaxf(p0, p1) : fmaxf(fmaxf(a[0], p0), p1);
       }
       pw[r >> 1] = cvt_pk_bf16(p0, p1);
       if constexpr (PP) lw[r >> 1] = residual(p0, p1, pw[r >> 1]);
     }
-    t32 = (a[0] + a[1]) + (a[2] + a[3]);
+    t32 = PP ? (a[0] + a[1]) + (a[2] + a[3]) : a[0];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       pj[h] = pack(pw, h);
@@ -350,6 +376,13 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     }
     m2 = m_new;
     softmax(sj, pj, pjl, t32);
+  };
+  // A tile that passed its check: PP adds the lane's fp32 sum to L32; with
+  // bf16 weights L32 keeps the lane's largest weight so far (the slow path
+  // rescales it with the sums).
+  auto fold = [&](float t32) __attribute__((always_inline)) {
+    if constexpr (PP) L32 += t32;
+    else L32 = fmaxf(L32, t32);
   };
 
   auto qk_mfma = [&](const lds_char* Kt, f32x16& sj) __attribute__((always_inline)) {
@@ -467,12 +500,35 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       wait_copies();
       __syncthreads();
       qk_mfma(Kl, s[0]);
+      constexpr int NPV = 2 * DB;   // PV(t-1) V fragments (PP: two MFMAs each)
+      constexpr int NV = NPV + (PP ? 0 : 2);  // ... and the row sums of P(t-1)
+      constexpr int NM = NV + KK;   // ... and QK^T(t+1)
+      // The last FWD_PF chunks of an iteration read the first V fragments of
+      // the next one's PV (V(t), published a pair earlier) into the same
+      // registers the next iteration starts from.
+      constexpr bool CARRY = NM % FWD_PF == 0 && FWD_PF <= NPV;
+      auto vfrag = [&](const lds_char* Vt, int i) __attribute__((always_inline)) -> bf16x8 {
+        const int half = i / DB, db = i % DB;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 0)));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 1)));
+        const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        return __builtin_bit_cast(bf16x8, v8);
+      };
+      bf16x8 ob[FWD_PF];
+      if constexpr (CARRY) {
+#pragma unroll
+        for (int i = 0; i < FWD_PF; ++i) ob[i] = vfrag(Vl + (NBUF - 1) * TB, i);
+      }
 
-      // Iteration t: copies of K(t+3), V(t+2); PV(t-1) and QK^T(t+1) on the
-      // matrix cores next to the softmax of tile t; the overflow check.
-      auto iter = [&](int t, auto P_, auto M_) __attribute__((always_inline)) {
+      // Iteration t: copies of K(t+5), V(t+4); PV(t-1) and QK^T(t+1) on the
+      // matrix cores next to the softmax of tile t; the overflow check; the
+      // barrier after odd iterations.
+      auto iter = [&](int t, auto P_, auto M_, auto B_) __attribute__((always_inline)) {
         constexpr int P = decltype(P_)::value;
         constexpr bool MASK = decltype(M_)::value;
+        constexpr bool BAR = decltype(B_)::value;
         // masked tiles: tile row u of this lane's row is visible when u < lim
         int lim = 0;
         if constexpr (MASK) {
@@ -483,19 +539,9 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         vcopy(t + V_AHEAD, (t + V_AHEAD) % NBUF);
         const lds_char* Vt = Vl + ((t + NBUF - 1) % NBUF) * TB;  // V(t-1)
         const lds_char* Kt = Kl + ((t + 1) % NBUF) * TB;         // K(t+1)
-        constexpr int NPV = 2 * DB;   // PV(t-1) V fragments (PP: two MFMAs each)
-        constexpr int NV = NPV + (PP ? 0 : 2);  // ... and the row sums of P(t-1)
-        constexpr int NM = NV + KK;   // ... and QK^T(t+1)
+        const lds_char* Vn = Vl + (t % NBUF) * TB;                // V(t), next PV
         auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-          if (i < NPV) {
-            const int half = i / DB, db = i % DB;
-            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 0)));
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(Vt + vaddr(half, db, 1)));
-            const i16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            return __builtin_bit_cast(bf16x8, v8);
-          }
+          if (i < NPV) return vfrag(Vt, i);
           if (i < NV) return ones8;
           const int kk = i - NV;
           return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
@@ -504,28 +550,34 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
         // The iteration is emitted as NM chunks, each one MFMA (its operands
         // read FWD_PF chunks ahead) and the softmax of some of the 16 score
         // elements of tile t; scheduling barriers keep the chunks in order, so
-        // the exponentials and sums issue while the matrix core is busy.
-        float a4[4], pe[16];
+        // the exponentials issue while the matrix core is busy.
+        float a4[4], pe[16];  // a4: running max of the weights (PP: four partial sums)
         uint32_t pw[8], lw[8];  // P of tile t, bf16 pairs (PP: and residual pairs)
         auto element = [&](int r) __attribute__((always_inline)) {
           if constexpr (MASK) {
             if ((r >> 2) * 8 + hi * 4 + (r & 3) >= lim) s[P][r] = -INFINITY;
           }
           pe[r] = __builtin_amdgcn_exp2f(fmaf(s[P][r], c_log2, -m2));
-          if (r < 4) a4[r] = pe[r];
-          else a4[r & 3] += pe[r];
+          if constexpr (PP) {
+            if (r < 4) a4[r] = pe[r];
+            else a4[r & 3] += pe[r];
+          } else if (r & 1) {
+            a4[0] = fmaxf(fmaxf(r == 1 ? L32 : a4[0], pe[r - 1]), pe[r]);
+          }
           if (r & 1) {
             pw[r >> 1] = cvt_pk_bf16(pe[r - 1], pe[r]);
             if constexpr (PP) lw[r >> 1] = residual(pe[r - 1], pe[r], pw[r >> 1]);
           }
         };
-        bf16x8 ob[FWD_PF];
+        if constexpr (!CARRY) {
 #pragma unroll
-        for (int i = 0; i < FWD_PF && i < NM; ++i) ob[i] = fetch(i);
+          for (int i = 0; i < FWD_PF && i < NM; ++i) ob[i] = fetch(i);
+        }
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
           const bf16x8 cur = ob[i % FWD_PF];
           if (i + FWD_PF < NM) ob[i % FWD_PF] = fetch(i + FWD_PF);
+          else if constexpr (CARRY) ob[i % FWD_PF] = vfrag(Vn, i + FWD_PF - NM);
           if (i < NPV) {
             const int half = i / DB, db = i % DB;
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[P ^ 1][half], acc[db], 0, 0,
@@ -545,39 +597,59 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
           for (int r = (16 * i) / NM; r < (16 * (i + 1)) / NM; ++r) element(r);
           __builtin_amdgcn_sched_barrier(0);
         }
-        ts32 = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        if constexpr (PP) ts32 = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        else ts32 = a4[0];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           pf[P][h] = pack(pw, h);
           if constexpr (PP) pl[P][h] = pack(lw, h);
         }
-        if (__ballot(ts32 > TILE_SUM_MAX)) reraise(s[P], pf[P], pl[P], ts32);
-        L32 += ts32;
-        wait_copies_but<2 * IPW>();
-        __syncthreads();
+        // With bf16 weights the max chain above started from L32, so
+        // without the slow path ts32 already is the new running max.
+        if (__ballot(ts32 > TILE_SUM_MAX)) {
+          reraise(s[P], pf[P], pl[P], ts32);
+          if constexpr (!PP) ts32 = fmaxf(ts32, L32);
+        }
+        if constexpr (PP) L32 += ts32;
+        else L32 = ts32;
+        if constexpr (BAR) {
+          // Only this pair's copies may still be in flight.  A plain
+          // s_barrier: the carried operand reads stay in flight across it
+          // (they read a tile that no copy of the next pair overwrites); the
+          // empty asm keeps the compiler from moving LDS accesses across it.
+          wait_copies_but<4 * IPW>();
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+        }
       };
+      using WITH_BAR = std::true_type;
+      using NO_BAR = std::false_type;
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
       using NOM = std::false_type;
-      // Pairs keep the tile parity static; masked pairs start at an even
-      // tile (masking a tile every row fully sees changes nothing).
+      // Pairs keep the tile parity static and end at the barrier; masked
+      // pairs start at an even tile (masking a tile every row fully sees
+      // changes nothing).  A last, unpaired iteration needs no barrier: what
+      // follows reads only tiles published before it, and waits for every
+      // copy before the closing barrier.
       const int n_plain = GL ? (n_main & ~1) : n_main;
       int t = 0;
       for (; t + 1 < n_plain; t += 2) {
-        iter(t, I0{}, NOM{});
-        iter(t + 1, I1{}, NOM{});
+        iter(t, I0{}, NOM{}, NO_BAR{});
+        iter(t + 1, I1{}, NOM{}, WITH_BAR{});
       }
       if constexpr (GL) {
         using MSK = std::true_type;
         for (; t + 1 < n_loop; t += 2) {
-          iter(t, I0{}, MSK{});
-          iter(t + 1, I1{}, MSK{});
+          iter(t, I0{}, MSK{}, NO_BAR{});
+          iter(t + 1, I1{}, MSK{}, WITH_BAR{});
         }
-        if (t < n_loop) iter(t, I0{}, MSK{});
+        if (t < n_loop) iter(t, I0{}, MSK{}, NO_BAR{});
       } else {
-        if (t < n_loop) iter(t, I0{}, NOM{});
+        if (t < n_loop) iter(t, I0{}, NOM{}, NO_BAR{});
       }
-      // PV(last); its V tile landed two iterations ago.
+      // PV(last); its V tile was published before the last pair.
       if (last & 1)
         pv_mfma(Vl + (last % NBUF) * TB, pf[1], pl[1]);
       else
@@ -622,7 +694,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
             }
           }
           reraise(s[0], pf[0], pl[0], ts32);
-          L32 += ts32;
+          fold(ts32);
           pv_mfma(Vt, pf[0], pl[0]);
         }
       }
@@ -645,7 +717,12 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
                           acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
         *reinterpret_cast<float4*>(orow + db * 32 + gq * 8 + hi * 4) = v;
       }
-    if (hi == 0) lse_bh[orow_i] = l32 > 0.f ? (m2 + __log2f(l32)) * LN2 : -INFINITY;
+    // bf16 weights: add back what rounding took off each lane's largest
+    // weight (the row's two lanes: xhalf_sum).
+    const float l_lse =
+        PP ? l32
+           : l16 + xhalf_sum(L32 - __builtin_bit_cast(float, cvt_pk_bf16(L32, 0.f) << 16));
+    if (hi == 0) lse_bh[orow_i] = l_lse > 0.f ? (m2 + __log2f(l_lse)) * LN2 : -INFINITY;
   }
 }
 

@@ -9,12 +9,13 @@ import torch
 
 from oracle import cpa_oracle
 
-# bf16 inputs vs the fp64 oracle: max |dO| <= 1e-2 and mean |dO| <= 1e-3 over
-# all checked elements; lse within 1e-3 * max(1, |lse|) (fp32 score
-# accumulation of large outlier logits); empty rows exactly (0, -inf).
+# bf16 inputs vs the fp64 oracle: max |d| <= 1e-2 and mean |d| <= 1e-3 over
+# all checked elements, for O and for lse alike (both are outputs of a
+# partial); empty rows exactly (0, -inf).  With bf16 weights lse is the log
+# of the sum of the rounded weights (the normaliser O uses), which a single
+# dominant key moves by up to ln(1 + 2^-9) ~ 2e-3.
 BF16_MAX_ABS = 1e-2
 BF16_MEAN_ABS = 1e-3
-LSE_REL = 1e-3
 # fp32 inputs: the pages' own check, assert_allclose(rtol=1e-5, atol=1e-6).
 F32_RTOL, F32_ATOL = 1e-5, 1e-6
 
@@ -96,8 +97,9 @@ def assert_bf16_close(O, lse, O_ref, lse_ref, what="", v_scale=1.0):
     assert mx <= mx_tol, f"{what}: max |dO| {mx:.3e} > {mx_tol}"
     assert mean <= mean_tol, f"{what}: mean |dO| {mean:.3e} > {mean_tol}"
     dl = np.abs(lse[fin] - lse_ref[fin])
-    bound = LSE_REL * np.maximum(1.0, np.abs(lse_ref[fin]))
-    assert np.all(dl <= bound), f"{what}: lse off by {float((dl / bound).max()):.2f}x tolerance"
+    if dl.size:
+        assert dl.max() <= BF16_MAX_ABS, f"{what}: max |dlse| {dl.max():.3e} > {BF16_MAX_ABS}"
+        assert dl.mean() <= BF16_MEAN_ABS, f"{what}: mean |dlse| {dl.mean():.3e} > {BF16_MEAN_ABS}"
     return mx, mean
 
 
