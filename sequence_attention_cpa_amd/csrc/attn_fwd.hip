@@ -525,21 +525,26 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       // Iteration t: copies of K(t+5), V(t+4); PV(t-1) and QK^T(t+1) on the
       // matrix cores next to the softmax of tile t; the overflow check; the
       // barrier after odd iterations.
-      auto iter = [&](int t, auto P_, auto M_, auto B_) __attribute__((always_inline)) {
+      auto iter = [&](int t, auto P_, auto M_, auto B_, auto PH_) __attribute__((always_inline)) {
         constexpr int P = decltype(P_)::value;
         constexpr bool MASK = decltype(M_)::value;
         constexpr bool BAR = decltype(B_)::value;
+        constexpr int PH = decltype(PH_)::value;  // t % NBUF when known, else -1
+        auto bufi = [&](int k) __attribute__((always_inline)) -> int {
+          if constexpr (PH >= 0) return (PH + k) % NBUF;
+          else return (t + k) % NBUF;
+        };
         // masked tiles: tile row u of this lane's row is visible when u < lim
         int lim = 0;
         if constexpr (MASK) {
           const int l = my_cnt - t * 32;
           lim = l < 0 ? 0 : (l > 32 ? 32 : l);
         }
-        kcopy(t + K_AHEAD, (t + K_AHEAD) % NBUF);
-        vcopy(t + V_AHEAD, (t + V_AHEAD) % NBUF);
-        const lds_char* Vt = Vl + ((t + NBUF - 1) % NBUF) * TB;  // V(t-1)
-        const lds_char* Kt = Kl + ((t + 1) % NBUF) * TB;         // K(t+1)
-        const lds_char* Vn = Vl + (t % NBUF) * TB;                // V(t), next PV
+        kcopy(t + K_AHEAD, bufi(K_AHEAD));
+        vcopy(t + V_AHEAD, bufi(V_AHEAD));
+        const lds_char* Vt = Vl + bufi(NBUF - 1) * TB;  // V(t-1)
+        const lds_char* Kt = Kl + bufi(1) * TB;         // K(t+1)
+        const lds_char* Vn = Vl + bufi(0) * TB;         // V(t), next PV
         auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
           if (i < NPV) return vfrag(Vt, i);
           if (i < NV) return ones8;
@@ -632,22 +637,37 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       // pairs start at an even tile (masking a tile every row fully sees
       // changes nothing).  A last, unpaired iteration needs no barrier: what
       // follows reads only tiles published before it, and waits for every
-      // copy before the closing barrier.
+      // copy before the closing barrier.  The unmasked loop runs a whole
+      // cycle of the NBUF buffers per trip, so every buffer index is a
+      // constant and each LDS address is a lane register plus an immediate
+      // offset (no address arithmetic per tile: 8 fewer VALU and about 15
+      // fewer SALU instructions; +2.5 % at the 128k share, +3 % at 12k).
       const int n_plain = GL ? (n_main & ~1) : n_main;
+      using DYN = std::integral_constant<int, -1>;
       int t = 0;
+      for (; t + NBUF <= n_plain; t += NBUF) {
+        iter(t, I0{}, NOM{}, NO_BAR{}, std::integral_constant<int, 0>{});
+        iter(t + 1, I1{}, NOM{}, WITH_BAR{}, std::integral_constant<int, 1>{});
+        iter(t + 2, I0{}, NOM{}, NO_BAR{}, std::integral_constant<int, 2>{});
+        iter(t + 3, I1{}, NOM{}, WITH_BAR{}, std::integral_constant<int, 3>{});
+        iter(t + 4, I0{}, NOM{}, NO_BAR{}, std::integral_constant<int, 4>{});
+        iter(t + 5, I1{}, NOM{}, WITH_BAR{}, std::integral_constant<int, 5>{});
+        iter(t + 6, I0{}, NOM{}, NO_BAR{}, std::integral_constant<int, 6>{});
+        iter(t + 7, I1{}, NOM{}, WITH_BAR{}, std::integral_constant<int, 7>{});
+      }
       for (; t + 1 < n_plain; t += 2) {
-        iter(t, I0{}, NOM{}, NO_BAR{});
-        iter(t + 1, I1{}, NOM{}, WITH_BAR{});
+        iter(t, I0{}, NOM{}, NO_BAR{}, DYN{});
+        iter(t + 1, I1{}, NOM{}, WITH_BAR{}, DYN{});
       }
       if constexpr (GL) {
         using MSK = std::true_type;
         for (; t + 1 < n_loop; t += 2) {
-          iter(t, I0{}, MSK{}, NO_BAR{});
-          iter(t + 1, I1{}, MSK{}, WITH_BAR{});
+          iter(t, I0{}, MSK{}, NO_BAR{}, DYN{});
+          iter(t + 1, I1{}, MSK{}, WITH_BAR{}, DYN{});
         }
-        if (t < n_loop) iter(t, I0{}, MSK{}, NO_BAR{});
+        if (t < n_loop) iter(t, I0{}, MSK{}, NO_BAR{}, DYN{});
       } else {
-        if (t < n_loop) iter(t, I0{}, NOM{}, NO_BAR{});
+        if (t < n_loop) iter(t, I0{}, NOM{}, NO_BAR{}, DYN{});
       }
       // PV(last); its V tile was published before the last pair.
       if (last & 1)
