@@ -252,6 +252,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   const int64_t qg = (int64_t)bh * Lrow + qmap(qrow_c);
   const float l2 = lse_ref(lse[qg]);
   const float dl = delta[qg];
+  f32x16 negdl;  // dP^T starts from -delta: dS = P (dP - delta) is one product
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negdl[r] = -dl;
 
   // Q and dO rows of this wave as B operands (lane: 8 columns of its query).
   bf16x8 qf[KK], df[KK];
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
     auto ds_rows = [&](int r0, int r1) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = r0; r < r1; r += 2) {
-        const float d0 = s[r] * (dp[r] - dl), d1 = s[r + 1] * (dp[r + 1] - dl);
+        const float d0 = s[r] * dp[r], d1 = s[r + 1] * dp[r + 1];
         dsf[r >> 3][(r >> 1) & 3] = cvt_pk_bf16(d0, d1);
       }
     };
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], i == 0 ? zero16 : s, 0, 0, 0);
       } else if (i < 2 * KK) {
         const int c = i - KK;
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, df[c], c == 0 ? zero16 : dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, df[c], c == 0 ? negdl : dp, 0, 0, 0);
 #pragma unroll
         for (int r = c * RPC; r < (c + 1) * RPC; ++r)
           s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l2));
