@@ -444,6 +444,22 @@ def test_share_forward_global_layout(case):
     assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr, str(case))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tiles", list(range(1, 11)))
+def test_share_forward_block_lengths(tiles, causal):
+    """Chunks of 1 to 10 key tiles (blocks of 2 to 20): the steady loop's
+    whole trips over the 8 LDS buffers, its remaining pairs, an unpaired last
+    tile and the masked pairs of crossing tiles all meet the oracle."""
+    B, H, N, D = 1, 2, 4, 128
+    L = 2 * N * 32 * tiles
+    Q, K, V = (rand((B, H, L, D), torch.bfloat16, 90 + i) for i in range(3))
+    Or, lr = cpa_oracle.attention(widen(Q), widen(K), widen(V), causal)
+    O, lse = cpa.share_forward(Q.to(DEV), K.to(DEV), V.to(DEV), N, causal)
+    torch.cuda.synchronize()
+    assert_bf16_close(O.cpu().double().numpy(), lse.cpu().double().numpy(), Or, lr,
+                      f"C={32 * tiles} causal={causal}")
+
+
 @pytest.mark.parametrize("case", SHARE_CASES, ids=[str(c) for c in SHARE_CASES])
 def test_share_forward_precise(case):
     """The precise-weight ring equals the oracle for every rank, and its O
