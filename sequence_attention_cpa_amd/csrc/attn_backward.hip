@@ -48,6 +48,8 @@ namespace {
 using namespace tile;
 
 constexpr int NTHREADS = 256;  // 4 waves
+// Query rows per rank from which the dQ pass runs 8-wave workgroups.
+constexpr int64_t kDqWideRows = 8192;
 constexpr int BM = 128;        // query rows (dQ pass) or key rows (dK/dV pass) per workgroup
 static_assert(BM == cpa::kMfmaRows && NTHREADS == cpa::kMfmaThreads,
               "the host checks launch sizes with these tile constants");
@@ -206,8 +208,13 @@ __device__ __forceinline__ int64_t zig_row(int r, int64_t u, int64_t Lr, int nbl
 // GL: Q, K, V, dO, lse, delta and dQ are the whole sequence in global token
 // order ([BH, nblk * Lq, ...]); the queries are rank `first`'s rows and K/V
 // block b is rank b's rows, all through zig_row.
-template <int D, bool GL>
-__global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
+// QW waves of 32 query rows per workgroup: 4 (two workgroups per CU), or 8
+// for long shares (one per CU), where every K/V tile staged in LDS then
+// serves twice the rows: half the copies per product, 1.1-1.4 % off the ring
+// backward at the 128k share; at 12k the wider workgroups' extra setup and
+// crossing tiles cost 1.7 %, so short shares keep 4.
+template <int D, bool GL, int QW>
+__global__ __launch_bounds__(64 * QW, 8 / QW) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ delta,
     const int64_t* __restrict__ q_off, const int64_t* __restrict__ k_off, float* __restrict__ dQ,
@@ -232,8 +239,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
   const int l32 = lane & 31;
   const int bh = blockIdx.x % BH;
   const int qt = n_qtiles - 1 - blockIdx.x / BH;
-  const int64_t q_base = (int64_t)qt * BM;
-  const int64_t last_row = (q_base + BM < Lq ? q_base + BM : Lq) - 1;
+  const int64_t q_base = (int64_t)qt * (32 * QW);
+  const int64_t last_row = (q_base + 32 * QW < Lq ? q_base + 32 * QW : Lq) - 1;
   const int64_t qrow = q_base + wv * 32 + l32;
   const int64_t qrow_c = qrow < Lq ? qrow : Lq - 1;
   const float c_log2 = scale * LOG2E;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dq_kernel(
       settle(df[kk]);
     }
   }
-  const CBTile<D, 4, 4> ta(wv, lane);
+  const CBTile<D, 4, QW> ta(wv, lane);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -965,12 +972,22 @@ hipError_t mfma_bwd(const void* Q, const void* K, const void* V, const void* dO,
                     float* dK, float* dV, int BH, int64_t Lq, int64_t Lk, int64_t kv_stride,
                     int64_t koff_stride, int nblk, int first, bool causal, float scale,
                     bool acc_dq, hipStream_t st) {
-  const int n_qtiles = (int)((Lq + BM - 1) / BM);
   const int n_ktiles = (int)((Lk + BM - 1) / BM);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, GL>), dim3((unsigned)(n_qtiles * BH)), dim3(NTHREADS), 0,
-                     st, (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, (const __bf16*)dO,
-                     lse, delta, q_off, k_off, dQ, BH, Lq, Lk, kv_stride, koff_stride, nblk,
-                     first, causal ? 1 : 0, scale, n_qtiles, acc_dq ? 1 : 0);
+  if (Lq >= kDqWideRows) {
+    const int n_qtiles = (int)((Lq + 255) / 256);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, GL, 8>), dim3((unsigned)(n_qtiles * BH)), dim3(512), 0,
+                       st, (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V,
+                       (const __bf16*)dO, lse, delta, q_off, k_off, dQ, BH, Lq, Lk, kv_stride,
+                       koff_stride, nblk, first, causal ? 1 : 0, scale, n_qtiles,
+                       acc_dq ? 1 : 0);
+  } else {
+    const int n_qtiles = (int)((Lq + BM - 1) / BM);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, GL, 4>), dim3((unsigned)(n_qtiles * BH)),
+                       dim3(NTHREADS), 0, st, (const __bf16*)Q, (const __bf16*)K,
+                       (const __bf16*)V, (const __bf16*)dO, lse, delta, q_off, k_off, dQ, BH,
+                       Lq, Lk, kv_stride, koff_stride, nblk, first, causal ? 1 : 0, scale,
+                       n_qtiles, acc_dq ? 1 : 0);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, GL>), dim3((unsigned)(nblk * n_ktiles * BH)),
