@@ -14,8 +14,10 @@
 //
 // Two matrix-core passes (bf16 inputs, D = 64 or 128), no atomics:
 //  * dQ pass: the forward kernel's shape.  A workgroup owns 128 query rows
-//    (32 per wave); K and V tiles of 32 keys stream through LDS (async copies,
-//    double buffered), Q and dO rows stay in registers.  Per tile:
+//    (32 per wave; 256 rows and 8 waves for shares of 8192 rows or more);
+//    K and V tiles of 32 keys stream through LDS (async copies into four
+//    buffers, one barrier per pair of tiles), Q and dO rows stay in
+//    registers; the dP accumulator starts from -delta.  Per tile:
 //    S^T = K Q^T and dP^T = V dO^T (each lane then holds 16 keys of ONE query,
 //    so lse and delta are one register each), P and dS on the VALU, then
 //    dQ^T += K^T dS^T with K^T read from LDS by ds_read_b64_tr_b16; the
@@ -224,8 +226,8 @@ __global__ __launch_bounds__(64 * QW, 8 / QW) void bwd_dq_kernel(
   constexpr int TB = G::TILE_BYTES;
   constexpr int KK = G::KK;
   constexpr int DB = G::DB;
-  __shared__ __attribute__((aligned(1024))) char k_lds_raw[2 * TB];
-  __shared__ __attribute__((aligned(1024))) char v_lds_raw[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char k_lds_raw[4 * TB];
+  __shared__ __attribute__((aligned(1024))) char v_lds_raw[4 * TB];
   lds_char* const Kl = (lds_char*)k_lds_raw;
   lds_char* const Vl = (lds_char*)v_lds_raw;
   // the same tiles as scalar LDS byte addresses for the copies
@@ -303,10 +305,13 @@ __global__ __launch_bounds__(64 * QW, 8 / QW) void bwd_dq_kernel(
   };
 
   auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
-    constexpr int P = decltype(P_)::value;
-    if (t + 1 < T) {
-      copy_kv(Kbh, Kbh_hi, t + 1, Kl_s + (P ^ 1) * TB);
-      copy_kv(Vbh, Vbh_hi, t + 1, Vl_s + (P ^ 1) * TB);
+    // Four K/V buffers, a barrier after every odd tile: tile t sits in buffer
+    // t % 4 (P), the pair (t, t+1) copies tiles t+2 and t+3 into the other
+    // two buffers and waits for them before its barrier.
+    constexpr int P = decltype(P_)::value;  // t % 4
+    if (t + 2 < T) {
+      copy_kv(Kbh, Kbh_hi, t + 2, Kl_s + ((P + 2) & 3) * TB);
+      copy_kv(Vbh, Vbh_hi, t + 2, Vl_s + ((P + 2) & 3) * TB);
     }
     const lds_char* Kt = Kl + P * TB;
     const lds_char* Vt = Vl + P * TB;
@@ -371,8 +376,10 @@ __global__ __launch_bounds__(64 * QW, 8 / QW) void bwd_dq_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_copies();
-    __syncthreads();
+    if constexpr (P & 1) {
+      wait_copies();
+      __syncthreads();
+    }
   };
 
   for (int sb = 0; sb < nblk; ++sb) {
@@ -411,14 +418,33 @@ __global__ __launch_bounds__(64 * QW, 8 / QW) void bwd_dq_kernel(
     T = (int)((n_hi + BN - 1) / BN);
     copy_kv(Kbh, Kbh_hi, 0, Kl_s);
     copy_kv(Vbh, Vbh_hi, 0, Vl_s);
+    if (T > 1) {
+      copy_kv(Kbh, Kbh_hi, 1, Kl_s + TB);
+      copy_kv(Vbh, Vbh_hi, 1, Vl_s + TB);
+    }
     wait_copies();
     __syncthreads();
-    int t = 0;
-    for (; t + 1 < T; t += 2) {
+    int t = 0;  // whole cycles of the four buffers, then a pair, then a single tile
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (; t + 3 < T; t += 4) {
       iter(t, I0{});
       iter(t + 1, I1{});
+      iter(t + 2, I2{});
+      iter(t + 3, I3{});
     }
-    if (t < T) iter(t, I0{});
+    if (t + 1 < T) {
+      iter(t, I0{});
+      iter(t + 1, I1{});
+      t += 2;
+    }
+    if (t < T) {  // a last single tile sits in buffer 0 or 2
+      if ((t & 3) == 0) iter(t, I0{});
+      else iter(t, I2{});
+    }
+    // the next block's first copies reuse the buffers
+    wait_copies();
+    __syncthreads();
   }
 
   if (qrow < Lq) {
