@@ -75,8 +75,9 @@
 //    fragment, once on each part.  hi + lo carries P to a relative 2^-16, so
 //    the bf16 rounding of P no longer limits O, and O is divided by the fp32
 //    sum instead (no matrix-core row sums); lse and the overflow check use
-//    that fp32 sum too (a sum above 2^40 takes the slow path).  It costs 8 MFMAs per tile
-//    (24 instead of 18 at D = 128) and about 40 VALU instructions.
+//    that fp32 sum too (a sum above 2^40 takes the slow path).  It costs 8
+//    MFMAs per tile (24 instead of 18 at D = 128) and about 40 VALU
+//    instructions.
 #include "cpa_internal.h"
 #include "mfma_tile.h"
 
