@@ -67,7 +67,12 @@
 //  * Global layout (cpa_share_forward): Q, K, V, O, lse are the whole sequence
 //    in token order and rank r's local row u is global row zig(r, u) (chunk r
 //    for u < C, chunk 2N-1-r after, C = L/(2N)); the positions are that same
-//    closed form, so no position table is read.
+//    closed form, so no position table is read.  With every block resident,
+//    the ring's N blocks are swept as one run of keys in global order: the
+//    same tiles as block by block, one copy prologue per workgroup instead of
+//    one per block, contiguous tile addresses, and every long workgroup of a
+//    head on the same tiles at the same time (L2 reuse).  +0.5 % at the 128k
+//    share, +3.4 % at 12k against the block-by-block ring (own block last).
 //  * Workgroups are issued longest-first (last query tiles first), heads
 //    fastest, so each XCD keeps working on the same heads' K/V in its L2.
 //  * Precise weights (PP, global layout only, opt-in): each P is split into
@@ -263,7 +268,8 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
   auto tile_src = [&](const __bf16* lo, const __bf16* hi_, int j)
                       __attribute__((always_inline)) -> const __bf16* {
     const int u0 = j * 32;
-    return ((GL && u0 >= C) ? hi_ : lo) + (int64_t)u0 * D;
+    (void)hi_;
+    return lo + (int64_t)u0 * D;
   };
   auto copy_full = [&](const __bf16* src, lds_char* dst) __attribute__((always_inline)) {
 #pragma unroll
@@ -418,14 +424,19 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     }
   };
 
-  for (int sb = 0; sb < nblk; ++sb) {
+  // GL: every block is resident and a token's position is its global index,
+  // so the ring's blocks are swept as ONE run of keys in global order
+  // (positions 0 .. L-1): the same tiles, one copy prologue instead of one
+  // per block, and contiguous tile addresses.
+  const int nsweep = GL ? 1 : nblk;
+  const int LkS = GL ? (int)Lrow : Lk;  // keys of one sweep (the rank-major ring: one block)
+  for (int sb = 0; sb < nsweep; ++sb) {
     const int blk = (first + 1 + sb) % nblk;
     if constexpr (GL) {
-      const int64_t lo_row = (int64_t)blk * C, hi_row = (int64_t)(2 * nblk - 1 - blk) * C - C;
-      Kbh = K + ((int64_t)bh * Lrow + lo_row) * D;
-      Vbh = V + ((int64_t)bh * Lrow + lo_row) * D;
-      Kbh_hi = K + ((int64_t)bh * Lrow + hi_row) * D;
-      Vbh_hi = V + ((int64_t)bh * Lrow + hi_row) * D;
+      Kbh = K + (int64_t)bh * Lrow * D;
+      Vbh = V + (int64_t)bh * Lrow * D;
+      Kbh_hi = Kbh;
+      Vbh_hi = Vbh;
     } else {
       Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
       Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
@@ -437,15 +448,15 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     // sees.  The same per wave for the tail.
     int n_main, n_tot, w_full, w_tot;
     if (!causal) {
-      n_main = w_full = Lk / 32;
-      n_tot = w_tot = (Lk + 31) / 32;
+      n_main = w_full = LkS / 32;
+      n_tot = w_tot = (LkS + 31) / 32;
     } else {
       int64_t c_g0, c_gl, c_w0, c_wl;
-      if constexpr (GL) {
-        c_g0 = zig_count_le(blk, nblk, C, pq_g0);
-        c_gl = zig_count_le(blk, nblk, C, pq_gl);
-        c_w0 = zig_count_le(blk, nblk, C, pq_w0);
-        c_wl = zig_count_le(blk, nblk, C, pq_wl);
+      if constexpr (GL) {  // keys at positions <= p: p + 1
+        c_g0 = pq_g0 + 1;
+        c_gl = pq_gl + 1;
+        c_w0 = pq_w0 + 1;
+        c_wl = pq_wl + 1;
       } else {
         const int64_t* kb_off = k_off + blk * koff_stride;
         c_g0 = count_le(kb_off, Lk, pq_g0);
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     const int n_loop = GL ? n_tot : n_main;
     int my_cnt = 0;
     if constexpr (GL) {
-      if (causal) my_cnt = (int)zig_count_le(blk, nblk, C, my_qpos);
+      if (causal) my_cnt = (int)(my_qpos + 1);
     }
 
     // ---- steady loop over tiles [0, n_loop): every wave sees [0, n_main) ----
@@ -704,10 +715,10 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int u = u0 + (r >> 2) * 8 + hi * 4 + (r & 3);
-              bool vis = u < Lk;
+              bool vis = u < LkS;
               if (causal && vis) {
                 int64_t kp;
-                if constexpr (GL) kp = zig(blk, u);
+                if constexpr (GL) kp = u;
                 else kp = k_off[blk * koff_stride + u];
                 vis = kp <= my_qpos;
               }
