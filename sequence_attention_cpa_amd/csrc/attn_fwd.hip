@@ -259,17 +259,11 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     coff[i] = crow[i] * RB + c * 16;
   }
 
-  // Current block: K/V bases (GL: rows below C from the first chunk, the rest
-  // from the second, whose base is already offset by -C rows).
+  // Current K/V bases: a rank-major block, or (GL) the head's whole sequence.
   const __bf16* Kbh = nullptr;
   const __bf16* Vbh = nullptr;
-  const __bf16* Kbh_hi = nullptr;
-  const __bf16* Vbh_hi = nullptr;
-  auto tile_src = [&](const __bf16* lo, const __bf16* hi_, int j)
-                      __attribute__((always_inline)) -> const __bf16* {
-    const int u0 = j * 32;
-    (void)hi_;
-    return lo + (int64_t)u0 * D;
+  auto tile_src = [&](const __bf16* base, int j) __attribute__((always_inline)) -> const __bf16* {
+    return base + (int64_t)(j * 32) * D;
   };
   auto copy_full = [&](const __bf16* src, lds_char* dst) __attribute__((always_inline)) {
 #pragma unroll
@@ -435,13 +429,9 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     if constexpr (GL) {
       Kbh = K + (int64_t)bh * Lrow * D;
       Vbh = V + (int64_t)bh * Lrow * D;
-      Kbh_hi = Kbh;
-      Vbh_hi = Vbh;
     } else {
       Kbh = K + blk * kv_stride + (int64_t)bh * Lk * D;
       Vbh = V + blk * kv_stride + (int64_t)bh * Lk * D;
-      Kbh_hi = Kbh;
-      Vbh_hi = Vbh;
     }
     // Tile counts.  n_main: tiles every row of the workgroup fully sees (the
     // first row sees the fewest); n_tot: tiles with a key any of its rows
@@ -487,11 +477,11 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       const int last = n_loop - 1;
       auto kcopy = [&](int j, int buf) __attribute__((always_inline)) {
         const int jj = j < last ? j : last;
-        copy_full(tile_src(Kbh, Kbh_hi, jj), Kl + buf * TB);
+        copy_full(tile_src(Kbh, jj), Kl + buf * TB);
       };
       auto vcopy = [&](int j, int buf) __attribute__((always_inline)) {
         const int jj = j < last ? j : last;
-        copy_full(tile_src(Vbh, Vbh_hi, jj), Vl + buf * TB);
+        copy_full(tile_src(Vbh, jj), Vl + buf * TB);
       };
 #pragma unroll
       for (int j = 0; j < K_AHEAD; ++j) kcopy(j, j % NBUF);
@@ -694,8 +684,8 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
     if (n_tot > n_loop) {
       auto tcopy = [&](int j) __attribute__((always_inline)) {
         const int buf = j % NBUF;
-        copy_any(tile_src(Kbh, Kbh_hi, j), j, Kl + buf * TB);
-        copy_any(tile_src(Vbh, Vbh_hi, j), j, Vl + buf * TB);
+        copy_any(tile_src(Kbh, j), j, Kl + buf * TB);
+        copy_any(tile_src(Vbh, j), j, Vl + buf * TB);
       };
       tcopy(n_loop);
       for (int t = n_loop; t < n_tot; ++t) {
