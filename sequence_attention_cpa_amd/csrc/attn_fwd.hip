@@ -460,12 +460,12 @@ __global__ __launch_bounds__(NTHREADS, 8 / WAVES) void attn_fwd_kernel(
       w_tot = __builtin_amdgcn_readfirstlane((int)((c_wl + 31) / 32));
     }
     if (w0 >= Lq) w_full = w_tot = 0;  // a wave past the last row stores nothing
-    if (n_tot == 0) continue;          // no row of the workgroup sees this block
-    // GL: every tile is whole (Lk is a multiple of 32), so the steady loop
-    // also runs the tiles that cross a row's causal bound, masking each
-    // element by the lane's count of visible keys in this block (keys are
-    // sorted by position); waves whose rows see none of such a tile compute
-    // it with every weight 0.  The rank-major path keeps them for the tail.
+    if (n_tot == 0) continue;          // no row of the workgroup sees this block (sweep)
+    // GL: every tile is whole (the sweep's L is a multiple of 32), so the
+    // steady loop also runs the tiles that cross a row's causal bound,
+    // masking each element by the lane's count of visible keys (keys are in
+    // position order); waves whose rows see none of such a tile compute it
+    // with every weight 0.  The rank-major path keeps them for the tail.
     const int n_loop = GL ? n_tot : n_main;
     int my_cnt = 0;
     if constexpr (GL) {
