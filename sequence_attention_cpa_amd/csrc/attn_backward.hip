@@ -696,19 +696,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     for (int i = 0; i < PF; ++i) ob[i] = fetch(i);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i == KK) {
-        __builtin_amdgcn_sched_barrier(0);
-        // hidden queries (tiles crossing a key's causal bound) get P = 0:
-        // tile row u is hidden when u < my_first - q0
-        if (q0 < m_hi) {
-          const int lim64 = my_first32 - (int)q0;
-          const int lim = lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (acc_row(r, hi) < lim) s[r] = -INFINITY;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
       const Ops cur = ob[i % PF];
       if (i + PF < NM) ob[i % PF] = fetch(i + PF);
       if (i >= KK && i < 3 * KK && ((i - KK) % KK * RPC) % 4 == 0) rg = cur.rv;
@@ -717,6 +704,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
       } else if (i < 2 * KK) {
         const int c = i - KK;
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a, cur.b, c == 0 ? zero16 : dp, 0, 0, 0);
+        if (c == 0) {
+          // The first dP product issues before the mask and the first
+          // exponentials, which wait for S's last product: the matrix core
+          // then has work while they wait.
+          __builtin_amdgcn_sched_barrier(0);
+          // hidden queries (tiles crossing a key's causal bound) get P = 0:
+          // tile row u is hidden when u < my_first - q0
+          if (q0 < m_hi) {
+            const int lim64 = my_first32 - (int)q0;
+            const int lim = lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (acc_row(r, hi) < lim) s[r] = -INFINITY;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
         // P of rows [c RPC, (c + 1) RPC), in place of S
 #pragma unroll
         for (int e = 0; e < RPC; e += 2) {
