@@ -634,11 +634,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
 
   auto iter = [&](int t, auto P_) __attribute__((always_inline)) {
     constexpr int P = decltype(P_)::value;
-    if (t + 1 < T) {
-      copy_q(Qbh, Qbh_hi, t + 1, Ql_s + (P ^ 1) * TB);
-      copy_q(Obh, Obh_hi, t + 1, Ol_s + (P ^ 1) * TB);
-      load_rows(t + 1);
-    }
     const lds_char* Qt = Ql + P * TB;
     const lds_char* Ot = Ol + P * TB;
     const int64_t q0 = (int64_t)t * BN;
@@ -694,6 +689,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void bwd_dkdv_kernel(
     Ops ob[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) ob[i] = fetch(i);
+    // The next tile's copies issue after the first operand reads, so that
+    // their address arithmetic runs while those reads are in flight.
+    if (t + 1 < T) {
+      copy_q(Qbh, Qbh_hi, t + 1, Ql_s + (P ^ 1) * TB);
+      copy_q(Obh, Obh_hi, t + 1, Ol_s + (P ^ 1) * TB);
+      load_rows(t + 1);
+    }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const Ops cur = ob[i % PF];
