@@ -5,7 +5,8 @@ K(t + K_AHEAD) and V(t + V_AHEAD) during iteration t, reads K(t+1), V(t-1)
 and (for the next iteration's first products) V(t), and meets at a barrier
 after every odd iteration; the dQ pass of the backward keeps K/V tile t in
 buffer t % 4, copies tile t + 2 during iteration t and meets after every odd
-tile.  Waves run freely between barriers, so a schedule is safe when, in every
+tile; the dK/dV pass keeps Q/dO tile t in buffer t % 2, copies tile t + 1
+during iteration t and meets after every tile.  Waves run freely between barriers, so a schedule is safe when, in every
 interval between two barriers:
   * each buffer read holds the tile the read expects, copied and waited for
     in an earlier interval (published by a barrier), and
@@ -154,3 +155,44 @@ def test_dq_pass_source_matches_the_model():
 @pytest.mark.parametrize("T", list(range(1, 41)))
 def test_dq_schedule(T):
     dq_pass(T).check(f"dQ T={T}")
+
+
+def dkdv_pass(T):
+    """The dK/dV pass over T query tiles (two Q/dO buffers)."""
+    s = Schedule()
+    s.copy("QO", 0, 0)
+    s.barrier()
+    for t in range(T):
+        s.read("QO", t % 2, t)  # the first operand reads, then the copy
+        if t + 1 < T:
+            s.copy("QO", (t + 1) % 2, t + 1)
+        s.barrier()
+    return s
+
+
+def test_dkdv_pass_source_matches_the_model():
+    """The dK/dV pass copies tile t + 1 into the other buffer after the first
+    operand reads and meets after every tile, as modelled."""
+    src = (CSRC / "attn_backward.hip").read_text()
+    assert "copy_q(Qbh, Qbh_hi, t + 1, Ql_s + (P ^ 1) * TB);" in src
+    assert "char q_lds_raw[2 * TB];" in src
+    body = src[src.index("void bwd_dkdv_kernel("):]
+    assert body.index("ob[i] = fetch(i);") < body.index("copy_q(Qbh, Qbh_hi, t + 1")
+
+
+@pytest.mark.parametrize("T", list(range(1, 21)))
+def test_dkdv_schedule(T):
+    dkdv_pass(T).check(f"dK/dV T={T}")
+
+
+def test_dkdv_schedule_catches_a_copy_into_the_read_buffer():
+    """The model is not vacuous: copying the next tile into the buffer being
+    read fails."""
+    s = Schedule()
+    s.copy("QO", 0, 0)
+    s.barrier()
+    s.read("QO", 0, 0)
+    s.copy("QO", 0, 1)
+    s.barrier()
+    with pytest.raises(AssertionError):
+        s.check("bad dK/dV")
