@@ -132,6 +132,7 @@ RANK_BWD_CASES = [
     (torch.bfloat16, 1, 1, 4096, 64, 64, True, "global"),  # 64 ranks, one tile per chunk
     (torch.bfloat16, 1, 1, 32768, 4, 128, True, "global"),  # 8192 rows per rank: 8-wave dQ pass
     (torch.bfloat16, 1, 1, 32768, 4, 64, True, True),
+    (torch.bfloat16, 1, 1, 32768, 4, 64, True, "global"),  # D = 64, 8-wave dQ on global order
     (torch.bfloat16, 1, 1, 33024, 4, 128, True, "global"),  # 8256 rows per rank: 8-wave dQ, ragged
     (torch.bfloat16, 1, 1, 33000, 4, 128, True, True),     # 8250 rows per rank, chunks of 4125
     (torch.bfloat16, 1, 2, 1000, 4, 128, True, True),   # 250 rows per rank: ragged tiles
